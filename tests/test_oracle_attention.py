@@ -1,0 +1,138 @@
+"""Pins of the oracle's dense / gather-sparse attention and the anchor-reuse residual
+(MC-Sparse summary page: grouping, residual and limitations paragraphs)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from sparse_attention_diffusion_amd import workloads
+
+
+def _qkv(n, d, seed, scale=1.0):
+    r = np.random.default_rng(seed)
+    return (scale * r.standard_normal((n, d)), scale * r.standard_normal((n, d)),
+            r.standard_normal((n, d)))
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=m, scale=scale)[0, 0].numpy()
+
+
+def test_dense_matches_torch_sdpa_fp64():
+    q, k, v = _qkv(90, 16, 0, 2.0)
+    assert np.allclose(ref.dense_attention(q, k, v, 0.25), _sdpa(q, k, v, 0.25), atol=1e-12)
+
+
+def test_dense_constant_values_and_identical_keys():
+    q, k, v = _qkv(30, 8, 1)
+    c = np.random.default_rng(2).standard_normal(8)
+    assert np.allclose(ref.dense_attention(q, k, np.tile(c, (30, 1)), 0.5), c, atol=1e-13)
+    same_k = np.tile(k[:1], (30, 1))
+    assert np.allclose(ref.dense_attention(q, same_k, v, 0.5), v.mean(axis=0), atol=1e-13)
+
+
+def test_dense_row_subset():
+    q, k, v = _qkv(50, 8, 3)
+    full = ref.dense_attention(q, k, v, 0.3)
+    rows = np.array([3, 49, 0, 17])
+    assert np.allclose(ref.dense_attention(q, k, v, 0.3, rows=rows), full[rows])
+
+
+def _groups_and_idx(n, c, kk, seed):
+    r = np.random.default_rng(seed)
+    perm = r.permutation(n)
+    g = -(-n // c)
+    idx = np.stack([np.sort(r.choice(n, kk, replace=False)) for _ in range(g)])
+    return perm, idx
+
+
+def test_sparse_matches_masked_sdpa():
+    n, c, kk = 70, 16, 9
+    q, k, v = _qkv(n, 8, 4, 1.5)
+    perm, idx = _groups_and_idx(n, c, kk, 5)
+    mask = np.zeros((n, n), dtype=bool)
+    for g in range(idx.shape[0]):
+        for t in perm[g * c:(g + 1) * c]:
+            mask[t, idx[g]] = True
+    want = _sdpa(q, k, v, 0.35, mask)
+    assert np.allclose(ref.sparse_attention(q, k, v, perm, idx, c, 0.35), want, atol=1e-12)
+
+
+def test_sparse_with_all_keys_is_dense():
+    n, c = 64, 16
+    q, k, v = _qkv(n, 8, 6)
+    perm = np.random.default_rng(7).permutation(n)
+    idx = np.tile(np.arange(n), (4, 1))
+    assert np.allclose(ref.sparse_attention(q, k, v, perm, idx, c, 0.4),
+                       ref.dense_attention(q, k, v, 0.4), atol=1e-13)
+
+
+def test_sparse_single_key_and_zero_queries():
+    n, c = 40, 8
+    q, k, v = _qkv(n, 8, 8)
+    perm, idx = _groups_and_idx(n, c, 1, 9)
+    out = ref.sparse_attention(q, k, v, perm, idx, c, 0.4)
+    for g in range(5):
+        assert np.allclose(out[perm[g * c:(g + 1) * c]], v[idx[g, 0]], atol=1e-15)
+    perm, idx = _groups_and_idx(n, c, 6, 10)
+    out = ref.sparse_attention(np.zeros_like(q), k, v, perm, idx, c, 0.4)
+    for g in range(5):
+        assert np.allclose(out[perm[g * c:(g + 1) * c]], v[idx[g]].mean(axis=0), atol=1e-14)
+
+
+def test_sparse_group_subset_leaves_other_rows_nan():
+    n, c = 48, 16
+    q, k, v = _qkv(n, 4, 11)
+    perm, idx = _groups_and_idx(n, c, 5, 12)
+    full = ref.sparse_attention(q, k, v, perm, idx, c, 0.5)
+    part = ref.sparse_attention(q, k, v, perm, idx, c, 0.5, groups=[1])
+    rows = perm[16:32]
+    assert np.allclose(part[rows], full[rows])
+    assert np.isnan(np.delete(part, rows, axis=0)).all()
+
+
+def _tiny_like(n=256, d=16, seed=0):
+    wl = workloads.Workload("t", (4, 8, n // 32), 1, d, "f32", 16, (0.2,), seed, 0.05, 1)
+    q, k, v = workloads.make_qkv(wl)
+    return wl, q[0], k[0], v[0]
+
+
+def test_anchor_sparse_plus_residual_is_dense():
+    wl, q, k, v = _tiny_like()
+    s = 1 / np.sqrt(16)
+    a = ref.anchor(q, k, v, 16, wl.topk(0.2), s)
+    assert np.allclose(a["o_sparse"] + a["resid"], a["o_dense"], atol=1e-13)
+    assert np.abs(a["resid"]).max() > 1e-3  # the dropped tail matters
+    assert a["idx"].shape == (16, wl.topk(0.2))
+
+
+def test_anchor_at_full_density_has_zero_residual():
+    wl, q, k, v = _tiny_like(seed=1)
+    a = ref.anchor(q, k, v, 16, 256, 0.25)
+    assert np.abs(a["resid"]).max() < 1e-13
+
+
+def test_reuse_without_drift_reproduces_dense():
+    wl, q, k, v = _tiny_like(seed=2)
+    s = 0.25
+    a = ref.anchor(q, k, v, 16, wl.topk(0.2), s)
+    out = ref.reuse(q, k, v, a["perm"], a["idx"], a["resid"], 16, s)
+    assert np.allclose(out, a["o_dense"], atol=1e-13)
+
+
+def test_reuse_with_drift_is_closer_to_dense_than_plain_sparse():
+    # residual paragraph: the residual changes less across steps than the output,
+    # so adding the stale residual beats dropping the tail (statistically, on the
+    # synthetic drift); checked here on the tiny workload as a sanity property.
+    wl = workloads.WORKLOADS["tiny"]
+    q0, k0, v0 = workloads.make_qkv(wl, step=0)
+    q1, k1, v1 = workloads.make_qkv(wl, step=1)
+    s = 1 / np.sqrt(wl.head_dim)
+    a = ref.anchor(q0[0], k0[0], v0[0], wl.group, wl.topk(0.2), s)
+    dense1 = ref.dense_attention(q1[0], k1[0], v1[0], s)
+    sparse1 = ref.sparse_attention(q1[0], k1[0], v1[0], a["perm"], a["idx"], wl.group, s)
+    reuse1 = ref.reuse(q1[0], k1[0], v1[0], a["perm"], a["idx"], a["resid"], wl.group, s)
+    assert np.abs(reuse1 - dense1).mean() < 0.5 * np.abs(sparse1 - dense1).mean()

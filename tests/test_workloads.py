@@ -1,0 +1,52 @@
+"""The seeded input generator: shapes, storage rounding and determinism."""
+import json
+import os
+
+import numpy as np
+import torch
+
+from sparse_attention_diffusion_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_tiny_case_figures_match_its_definition():
+    with open(os.path.join(GOLDEN, "workload_figures.json")) as f:
+        fig = json.load(f)["tiny_case"]
+    wl = W.WORKLOADS["tiny"]
+    assert wl.n == fig["n"] and wl.group == fig["group"]
+    assert wl.groups == fig["groups"]
+    assert wl.topk(fig["density"]) == fig["topk"]
+
+
+def test_grid_token_order_is_row_major():
+    c = W.grid_coords((2, 3, 4))
+    assert c.shape == (24, 3)
+    t, y, x = 1, 2, 3
+    assert (c[(t * 3 + y) * 4 + x] == [t, y, x]).all()
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
+    x[:4] = [1.00390625, 1.01171875, -2.00390625, 0.0]  # exact ties
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert (W.round_bf16(x) == want).all()
+
+
+def test_generator_is_deterministic_and_drifts():
+    wl = W.WORKLOADS["tiny"]
+    a = W.make_qkv(wl)
+    b = W.make_qkv(wl)
+    for x, y in zip(a, b):
+        assert (x == y).all()
+    c = W.make_qkv(wl, step=1)
+    dq = (c[0] - a[0]).std()
+    assert 0.03 < dq < 0.07  # one random-walk step of sigma 0.05
+
+
+def test_feature_statistics():
+    wl = W.WORKLOADS["tiny"]
+    q, k, v = W.make_qkv(wl)
+    assert q.shape == (1, 1024, 64) and q.dtype == np.float32
+    # unit-variance features plus 0.5^2 noise
+    assert abs(q.var() - 1.25) < 0.1 and abs(v.var() - 1.0) < 0.05
