@@ -1,0 +1,182 @@
+"""MC-Sparse hot path on MI355X: Python binding of libmcs.so.
+
+Every function marshals torch tensors (device memory, current HIP stream) into
+the C ABI declared in include/mcs.h; all arithmetic runs in the library's HIP
+kernels.  There is no fallback: a missing or failing library raises McsError.
+
+Tensor conventions (see include/mcs.h): q, k, v, outputs and residuals are
+[H, N, D] float32 or bfloat16 CUDA tensors; perm is int32 [H, N] (slot ->
+token); idx is int32 [H, G, kpad] (ascending kept keys, -1 padded),
+G = ceil(N / 64); lse is float32 [H, N].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _abi
+from ._abi import (MCS_BF16, MCS_COPY_D2D, MCS_COPY_D2H, MCS_COPY_H2D, MCS_F32, MCS_OP_ANCHOR,  # noqa: F401
+                   MCS_OP_GROUP, MCS_OP_SELECT, McsDims, McsError)
+
+GROUP = 64
+POWER_ITERS = 32
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def kpad_for(topk: int) -> int:
+    return ((topk + 31) // 32) * 32
+
+
+def make_dims(q, topk: int = 1, kpad: int | None = None, scale: float | None = None,
+              power_iters: int = POWER_ITERS) -> McsDims:
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [H, N, D]")
+    h, n, d = q.shape
+    if q.dtype == torch.bfloat16:
+        dt = MCS_BF16
+    elif q.dtype == torch.float32:
+        dt = MCS_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return McsDims(heads=h, n=n, head_dim=d, group=GROUP, topk=topk,
+                   kpad=kpad_for(topk) if kpad is None else kpad, dtype=dt,
+                   power_iters=power_iters, scale=(1.0 / math.sqrt(d)) if scale is None else scale)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _check_same(ref, *ts):
+    for t in ts:
+        if t is not None and (t.device != ref.device or t.shape != ref.shape or t.dtype != ref.dtype):
+            raise ValueError("q, k, v (and outputs) must share device, shape and dtype")
+
+
+def mcs_workspace_bytes(dims: McsDims, op: int, heads_per_pass: int = 0) -> int:
+    lib = _abi.load()
+    out = ctypes.c_size_t(0)
+    _abi.check(lib.mcs_workspace_bytes(ctypes.byref(dims), op, heads_per_pass, ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(dims, op, device, ws, heads_per_pass):
+    torch = _torch()
+    need = mcs_workspace_bytes(dims, op, heads_per_pass)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws
+
+
+def mcs_group(q, power_iters: int = POWER_ITERS, ws=None, perm=None):
+    """PDDP grouping: returns perm int32 [H, N]."""
+    torch = _torch()
+    lib = _abi.load()
+    d = make_dims(q, power_iters=power_iters)
+    if perm is None:
+        perm = torch.empty(q.shape[:2], dtype=torch.int32, device=q.device)
+    ws = _workspace(d, MCS_OP_GROUP, q.device, ws, 0)
+    _abi.check(lib.mcs_group(ctypes.byref(d), _ptr(q), _ptr(perm), _ptr(ws), ws.numel(), _stream(q.device)))
+    return perm
+
+
+def mcs_select(q, k, perm, topk: int, lse=None, ws=None, heads_per_pass: int = 0, idx=None):
+    """Two-pass exact top-K: returns idx int32 [H, G, kpad]."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k)
+    d = make_dims(q, topk=topk)
+    g = -(-q.shape[1] // GROUP)
+    if idx is None:
+        idx = torch.empty((q.shape[0], g, d.kpad), dtype=torch.int32, device=q.device)
+    ws = _workspace(d, MCS_OP_SELECT, q.device, ws, heads_per_pass)
+    _abi.check(lib.mcs_select(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(perm), _ptr(lse), _ptr(idx), _ptr(ws),
+                              ws.numel(), _stream(q.device)))
+    return idx
+
+
+def mcs_dense_attn(q, k, v, want_lse: bool = False, o=None):
+    """Dense attention: returns (o, lse or None)."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k, v)
+    d = make_dims(q)
+    if o is None:
+        o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if want_lse else None
+    _abi.check(lib.mcs_dense_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _stream(q.device)))
+    return o, lse
+
+
+def mcs_sparse_attn(q, k, v, perm, idx, topk: int, resid_add=None, o=None):
+    """Gather-sparse attention (+ optional residual): returns o [H, N, D]."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k, v, resid_add)
+    d = make_dims(q, topk=topk, kpad=idx.shape[2])
+    if o is None:
+        o = torch.empty_like(q)
+    _abi.check(lib.mcs_sparse_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(idx),
+                                   _ptr(resid_add), _ptr(o), _stream(q.device)))
+    return o
+
+
+def mcs_anchor(q, k, v, topk: int, power_iters: int = POWER_ITERS, want_lse: bool = False, ws=None,
+               heads_per_pass: int = 0, out=None):
+    """Anchor step: returns dict(perm, idx, resid, o_dense, lse)."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k, v)
+    d = make_dims(q, topk=topk, power_iters=power_iters)
+    h, n, _ = q.shape
+    g = -(-n // GROUP)
+    if out is None:
+        out = dict(perm=torch.empty((h, n), dtype=torch.int32, device=q.device),
+                   idx=torch.empty((h, g, d.kpad), dtype=torch.int32, device=q.device),
+                   resid=torch.empty_like(q), o_dense=torch.empty_like(q),
+                   lse=torch.empty((h, n), dtype=torch.float32, device=q.device) if want_lse else None)
+    ws = _workspace(d, MCS_OP_ANCHOR, q.device, ws, heads_per_pass)
+    _abi.check(lib.mcs_anchor(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(out["perm"]), _ptr(out["idx"]),
+                              _ptr(out["resid"]), _ptr(out["o_dense"]), _ptr(out.get("lse")), _ptr(ws),
+                              ws.numel(), _stream(q.device)))
+    return out
+
+
+def mcs_reuse(q, k, v, perm, idx, resid, topk: int, o=None):
+    """Reuse step: sparse attention with cached perm/idx plus the cached residual."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k, v, resid)
+    d = make_dims(q, topk=topk, kpad=idx.shape[2])
+    if o is None:
+        o = torch.empty_like(q)
+    _abi.check(lib.mcs_reuse(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(idx), _ptr(resid),
+                             _ptr(o), _stream(q.device)))
+    return o
+
+
+def mcs_copy_async(dst, src, kind: int, stream=None, event=None):
+    """Enqueue a byte copy of src into dst on `stream` (default: current) and record `event`."""
+    torch = _torch()
+    lib = _abi.load()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src sizes differ")
+    dev = src.device if src.is_cuda else dst.device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    ev = ctypes.c_void_p(event.cuda_event) if event is not None else None
+    _abi.check(lib.mcs_copy_async(_ptr(dst), _ptr(src), nbytes, kind, ctypes.c_void_p(s.cuda_stream), ev))

@@ -1,0 +1,303 @@
+// C ABI of the MC-Sparse hot path: host-side validation, workspace carve-up and
+// the composition of the kernels into the anchor and reuse steps.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/mcs.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MCS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_size(int32_t dtype) { return dtype == MCS_BF16 ? 2 : 4; }
+
+int groups_of(const mcs_dims* d) { return (d->n + d->group - 1) / d->group; }
+
+// Shape checks shared by every op.  need_topk: K/kpad are used by the op.
+int check_dims(const mcs_dims* d, bool need_topk) {
+  if (!d) return fail(MCS_EINVAL, "dims is NULL");
+  if (d->heads < 1 || d->n < 1) return fail(MCS_EINVAL, "heads (%d) and n (%d) must be >= 1", d->heads, d->n);
+  if (d->dtype != MCS_F32 && d->dtype != MCS_BF16) return fail(MCS_EUNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(MCS_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->group != 64) return fail(MCS_EUNSUPPORTED, "group size %d not supported (must be 64)", d->group);
+  if (!(d->scale > 0.0f) || !isfinite(d->scale)) return fail(MCS_EINVAL, "scale must be finite and > 0");
+  const size_t head_bytes = (size_t)d->n * d->head_dim * elem_size(d->dtype);
+  if (head_bytes >= ((size_t)1 << 31)) return fail(MCS_EINVAL, "one head of q/k/v exceeds 2 GiB");
+  if ((size_t)d->heads * (size_t)groups_of(d) >= ((size_t)1 << 31)) return fail(MCS_EINVAL, "too many groups");
+  if (need_topk) {
+    if (d->topk < 1 || d->topk > d->n) return fail(MCS_EINVAL, "topk %d outside [1, n=%d]", d->topk, d->n);
+    if (d->kpad < d->topk || d->kpad % 32 != 0)
+      return fail(MCS_EINVAL, "kpad %d must be >= topk (%d) and a multiple of 32", d->kpad, d->topk);
+  }
+  return MCS_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(MCS_EINVAL, "%s is NULL", name);
+  if (((uintptr_t)p) % align != 0) return fail(MCS_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return MCS_OK;
+}
+
+#define CHECK(x)               \
+  do {                         \
+    int _rc = (x);             \
+    if (_rc != MCS_OK) return _rc; \
+  } while (0)
+
+size_t stats_bytes(const mcs_dims* d) { return align256((size_t)d->heads * d->n * 8); }
+size_t mass_bytes_per_head(const mcs_dims* d) { return align256((size_t)groups_of(d) * d->n * 4); }
+size_t group_ws(const mcs_dims* d) { return mcs::pddp_workspace_bytes(d->heads, d->n, d->head_dim, d->group); }
+size_t select_ws(const mcs_dims* d, int hpp) { return stats_bytes(d) + (size_t)hpp * mass_bytes_per_head(d); }
+
+mcs::AttnArgs attn_args(const mcs_dims* d, const void* q, const void* k, const void* v) {
+  mcs::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.H = d->heads;
+  a.N = d->n;
+  a.G = groups_of(d);
+  a.nkeys = d->n;
+  a.kpad = d->kpad;
+  a.c = (float)((double)d->scale * 1.4426950408889634);
+  return a;
+}
+
+// Pass 2 + top-K over head chunks; stats (from pass 1 or the dense pass) or lse.
+int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const float2* stats,
+               const float* lse, int32_t* idx, float* mass, int hpp, hipStream_t s) {
+  const int G = groups_of(d);
+  for (int h0 = 0; h0 < d->heads; h0 += hpp) {
+    const int hc = d->heads - h0 < hpp ? d->heads - h0 : hpp;
+    mcs::MassArgs m{};
+    m.q = q;
+    m.k = k;
+    m.perm = perm;
+    m.stats = stats;
+    m.lse = lse;
+    m.mass = mass;
+    m.h0 = h0;
+    m.hcount = hc;
+    m.N = d->n;
+    m.G = G;
+    m.c = (float)((double)d->scale * 1.4426950408889634);
+    hipError_t e = mcs::launch_group_mass(m, d->dtype, d->head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "group mass launch");
+    mcs::TopkArgs t{};
+    t.mass = mass;
+    t.idx = idx + (size_t)h0 * G * d->kpad;
+    t.rows = hc * G;
+    t.N = d->n;
+    t.K = d->topk;
+    t.kpad = d->kpad;
+    e = mcs::launch_topk(t, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  }
+  return MCS_OK;
+}
+
+int heads_per_pass(const mcs_dims* d, size_t ws_bytes) {
+  const size_t fixed = stats_bytes(d), per = mass_bytes_per_head(d);
+  if (ws_bytes < fixed + per) return 0;
+  size_t hpp = (ws_bytes - fixed) / per;
+  return hpp > (size_t)d->heads ? d->heads : (int)hpp;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mcs_abi_version(void) { return MCS_ABI_VERSION; }
+
+const char* mcs_last_error(void) { return g_err.c_str(); }
+
+int mcs_workspace_bytes(const mcs_dims* d, int32_t op, int32_t hpp, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MCS_EINVAL, "bytes is NULL");
+  CHECK(check_dims(d, false));
+  if (hpp < 0) return fail(MCS_EINVAL, "heads_per_pass must be >= 0");
+  const int h = (hpp == 0 || hpp > d->heads) ? d->heads : hpp;
+  switch (op) {
+    case MCS_OP_GROUP: *bytes = group_ws(d); return MCS_OK;
+    case MCS_OP_SELECT: *bytes = select_ws(d, h); return MCS_OK;
+    case MCS_OP_ANCHOR: {
+      const size_t a = group_ws(d), b = select_ws(d, h);
+      *bytes = a > b ? a : b;
+      return MCS_OK;
+    }
+    default: return fail(MCS_EINVAL, "unknown op %d", op);
+  }
+}
+
+int mcs_group(const mcs_dims* d, const void* q, int32_t* perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, false));
+  if (d->power_iters < 1 || d->power_iters > 1024) return fail(MCS_EINVAL, "power_iters %d outside [1, 1024]", d->power_iters);
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(ws, 256, "workspace"));
+  if (ws_bytes < group_ws(d)) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, group_ws(d));
+  mcs::PddpArgs a{q, perm, ws, d->heads, d->n, d->head_dim, d->group, d->power_iters};
+  hipError_t e = mcs::launch_pddp(a, d->dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "pddp launch");
+  return MCS_OK;
+}
+
+int mcs_select(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const float* lse,
+               int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(idx, 16, "idx"));
+  if (lse) CHECK(check_ptr(lse, 4, "lse"));
+  CHECK(check_ptr(ws, 256, "workspace"));
+  const int hpp = heads_per_pass(d, ws_bytes);
+  if (hpp < 1) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, select_ws(d, 1));
+  float2* stats = (float2*)ws;
+  float* mass = (float*)((char*)ws + stats_bytes(d));
+  if (!lse) {
+    mcs::AttnArgs a = attn_args(d, q, k, nullptr);
+    a.stats = stats;
+    hipError_t e = mcs::launch_attention(a, d->dtype, d->head_dim, false, mcs::EPI_PLAIN, false, stream);
+    if (e != hipSuccess) return hip_fail(e, "selection pass 1 launch");
+  }
+  return run_select(d, q, k, perm, lse ? nullptr : stats, lse, idx, mass, hpp, stream);
+}
+
+int mcs_dense_attn(const mcs_dims* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                   hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, false));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(o, 16, "o"));
+  if (lse) CHECK(check_ptr(lse, 4, "lse"));
+  mcs::AttnArgs a = attn_args(d, q, k, v);
+  a.o = o;
+  a.lse = lse;
+  hipError_t e = mcs::launch_attention(a, d->dtype, d->head_dim, false, mcs::EPI_PLAIN, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  return MCS_OK;
+}
+
+int mcs_sparse_attn(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
+                    const int32_t* idx, const void* resid_add, void* o, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(idx, 16, "idx"));
+  CHECK(check_ptr(o, 16, "o"));
+  if (resid_add) CHECK(check_ptr(resid_add, 16, "resid_add"));
+  mcs::AttnArgs a = attn_args(d, q, k, v);
+  a.perm = perm;
+  a.idx = idx;
+  a.nkeys = d->topk;
+  a.rin = resid_add;
+  a.o = o;
+  hipError_t e = mcs::launch_attention(a, d->dtype, d->head_dim, true, resid_add ? mcs::EPI_ADD : mcs::EPI_PLAIN,
+                                       true, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+  return MCS_OK;
+}
+
+int mcs_anchor(const mcs_dims* d, const void* q, const void* k, const void* v, int32_t* perm, int32_t* idx,
+               void* resid, void* o_dense, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  if (d->power_iters < 1 || d->power_iters > 1024) return fail(MCS_EINVAL, "power_iters %d outside [1, 1024]", d->power_iters);
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(idx, 16, "idx"));
+  CHECK(check_ptr(resid, 16, "resid"));
+  CHECK(check_ptr(o_dense, 16, "o_dense"));
+  if (lse) CHECK(check_ptr(lse, 4, "lse"));
+  CHECK(check_ptr(ws, 256, "workspace"));
+  if (ws_bytes < group_ws(d)) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, group_ws(d));
+  const int hpp = heads_per_pass(d, ws_bytes);
+  if (hpp < 1) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, select_ws(d, 1));
+  // 1. grouping
+  mcs::PddpArgs pa{q, perm, ws, d->heads, d->n, d->head_dim, d->group, d->power_iters};
+  hipError_t e = mcs::launch_pddp(pa, d->dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "pddp launch");
+  // 2. dense attention; its row statistics double as selection pass 1
+  float2* stats = (float2*)ws;
+  float* mass = (float*)((char*)ws + stats_bytes(d));
+  mcs::AttnArgs a = attn_args(d, q, k, v);
+  a.o = o_dense;
+  a.lse = lse;
+  a.stats = stats;
+  e = mcs::launch_attention(a, d->dtype, d->head_dim, false, mcs::EPI_PLAIN, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  // 3. selection pass 2 and top-K
+  CHECK(run_select(d, q, k, perm, stats, nullptr, idx, mass, hpp, stream));
+  // 4. residual = dense - sparse
+  mcs::AttnArgs sa = attn_args(d, q, k, v);
+  sa.perm = perm;
+  sa.idx = idx;
+  sa.nkeys = d->topk;
+  sa.rin = o_dense;
+  sa.o = resid;
+  e = mcs::launch_attention(sa, d->dtype, d->head_dim, true, mcs::EPI_RESID, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "residual launch");
+  return MCS_OK;
+}
+
+int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
+              const int32_t* idx, const void* resid, void* o, hipStream_t stream) {
+  g_err.clear();
+  if (!resid) return fail(MCS_EINVAL, "resid is NULL");
+  return mcs_sparse_attn(d, q, k, v, perm, idx, resid, o, stream);
+}
+
+int mcs_copy_async(void* dst, const void* src, size_t bytes, int32_t kind, hipStream_t stream, hipEvent_t done) {
+  g_err.clear();
+  if (!dst || !src) return fail(MCS_EINVAL, "dst/src is NULL");
+  hipMemcpyKind k;
+  switch (kind) {
+    case MCS_COPY_H2D: k = hipMemcpyHostToDevice; break;
+    case MCS_COPY_D2H: k = hipMemcpyDeviceToHost; break;
+    case MCS_COPY_D2D: k = hipMemcpyDeviceToDevice; break;
+    default: return fail(MCS_EINVAL, "unknown copy kind %d", kind);
+  }
+  if (bytes) {
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, k, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  }
+  if (done) {
+    hipError_t e = hipEventRecord(done, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return MCS_OK;
+}
+
+}  // extern "C"

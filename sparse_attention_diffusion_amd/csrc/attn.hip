@@ -1,0 +1,411 @@
+// Flash-style attention kernels of the MC-Sparse hot path for gfx950.
+//
+// One wavefront owns one query group of C = 64 queries (PDDP groups on the sparse
+// path, consecutive token blocks on the dense path) and walks that group's key
+// list 32 keys at a time:
+//   * gather-sparse (MC-Sparse summary page, grouping paragraph): the key list is
+//     the group's row of int32 indices; every K/V row is fetched straight from
+//     global memory by index (no block repacking), so a group's keys may lie
+//     anywhere in the sequence;
+//   * dense (limitations paragraph: anchors still run full attention): the key
+//     list is 0..N-1.
+// Per 32-key step the wave computes S^T = K_step * Q_group^T with
+// v_mfma_f32_32x32x16_bf16 (fp32 inputs: 32x32x2_f32), so each lane owns one
+// query column and the online softmax needs a single cross-half exchange
+// (v_permlane32_swap); then O += P * V_step on the same MFMA shape.  P never
+// leaves registers: the accumulator layout of S^T is already the A-operand
+// layout of the PV product once the step's key order is fixed accordingly.
+//
+// Epilogues (residual paragraph): plain O, O + cached residual (reuse step),
+// or dense output minus O (the anchor's residual).  A variant without the PV
+// product produces the per-row softmax statistics (selection pass 1).
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mcs {
+
+namespace {
+
+// Lane-level tile bookkeeping of one 32-key step.
+//   A-row m of S^T (lane m%32 loads its K row) holds step entry
+//     e(m) = 16*((m/4)%2) + 4*(m/8) + m%4,
+//   which makes accumulator register r of lane half hf hold entry 16*hf + r.
+//   The PV product then consumes registers 8*ks..8*ks+7 as its k-slots, and the
+//   V operand of lane half hf needs entries 16*hf + 8*ks + t: 16 consecutive
+//   entries per lane half.
+__device__ __forceinline__ int a_row_entry(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+template <typename T, int D>
+struct Tile {
+  static constexpr bool F32 = std::is_same<T, float>::value;
+  static constexpr int ES = sizeof(T);
+  static constexpr int ROWB = D * ES;
+  // K/Q operand: each lane holds half a row (bf16: dims 16s+8hf..+7 for step s;
+  // fp32: dims (D/2)*hf + s), fetched as 16-byte chunks.
+  static constexpr int KCH = ROWB / 2 / 16;          // 16-byte chunks per lane
+  static constexpr int KSTRIDE = F32 ? 16 : 32;      // byte stride between chunks
+  static constexpr int QK_STEPS = F32 ? D / 2 : D / 16;
+  // V operand: each lane fetches VEC consecutive dims of each of its 16 entries.
+  static constexpr int VEC = D / 32;
+  static constexpr int VBYTES = VEC * ES;
+  static constexpr int VW = VBYTES / 4;              // dwords per V fetch
+  static_assert(VW == 1 || VW == 2 || VW == 4, "V fetch width");
+
+  __device__ static uint32_t khalf_off(int hf) { return F32 ? (uint32_t)(D / 2 * 4 * hf) : (uint32_t)(16 * hf); }
+};
+
+template <int VW>
+struct VRaw;
+template <> struct VRaw<1> { uint32_t w[1]; };
+template <> struct VRaw<2> { uint32_t w[2]; };
+template <> struct VRaw<4> { uint32_t w[4]; };
+
+template <typename T, int D>
+struct KV {
+  using TL = Tile<T, D>;
+  u32x4 k[TL::KCH];
+  VRaw<TL::VW> v[16];
+};
+
+struct Idx {
+  int k;       // key of this lane's A-row
+  int v[16];   // keys of entries 16*hf + 0..15
+};
+
+template <int VW>
+__device__ __forceinline__ VRaw<VW> vload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  VRaw<VW> x;
+  if constexpr (VW == 1) {
+    x.w[0] = bload32(r, off);
+  } else if constexpr (VW == 2) {
+    u32x2 t = bload64(r, off);
+    x.w[0] = t[0];
+    x.w[1] = t[1];
+  } else {
+    u32x4 t = bload128(r, off);
+    x.w[0] = t[0]; x.w[1] = t[1]; x.w[2] = t[2]; x.w[3] = t[3];
+  }
+  return x;
+}
+
+template <bool GATHER>
+__device__ __forceinline__ void load_idx(Idx& ix, __amdgpu_buffer_rsrc_t ridx, int t0, int nkeys, int lm, int hf) {
+  if constexpr (GATHER) {
+    const int ek = t0 + a_row_entry(lm);
+    int kk = (int)bload32(ridx, (uint32_t)ek * 4u);
+    ix.k = (ek < nkeys && kk > 0) ? kk : 0;  // entries past K hold -1
+    const int ev = t0 + 16 * hf;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 w = bload128(ridx, (uint32_t)(ev + 4 * c) * 4u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int kv = (int)w[j];
+        ix.v[4 * c + j] = (ev + 4 * c + j < nkeys && kv > 0) ? kv : 0;
+      }
+    }
+  } else {
+    const int ek = t0 + a_row_entry(lm);
+    ix.k = ek < nkeys ? ek : 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int e = t0 + 16 * hf + j;
+      ix.v[j] = e < nkeys ? e : 0;
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_k(KV<T, D>& b, const Idx& ix, __amdgpu_buffer_rsrc_t rk, int hf) {
+  using TL = Tile<T, D>;
+  const uint32_t kb = (uint32_t)ix.k * TL::ROWB + TL::khalf_off(hf);
+#pragma unroll
+  for (int c = 0; c < TL::KCH; ++c) b.k[c] = bload128(rk, kb + c * TL::KSTRIDE);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_v(KV<T, D>& b, const Idx& ix, __amdgpu_buffer_rsrc_t rv, int lm) {
+  using TL = Tile<T, D>;
+  const uint32_t lo = (uint32_t)lm * TL::VBYTES;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) b.v[j] = vload<TL::VW>(rv, (uint32_t)ix.v[j] * TL::ROWB + lo);
+}
+
+// Component c (0..VEC-1) of fetched V data as a 16-bit (bf16) half-word source.
+template <int VW>
+__device__ __forceinline__ uint32_t vword(const VRaw<VW>& x, int c) { return x.w[c >> 1]; }
+
+template <typename T, int D, bool PV>
+struct State {
+  using TL = Tile<T, D>;
+  f32x16 o[2][TL::VEC];
+  float m[2];   // running offset, log2 units (scaled max), per query column
+  float l[2];   // running sum of exp2(s*c - m)
+};
+
+// S^T of one 32-key step (rows: the step's keys, columns: the group's 64 queries).
+template <typename T, int D>
+__device__ __forceinline__ void qk(f32x16 (&s)[2], const KV<T, D>& b, const u32x4 (&q)[2][Tile<T, D>::KCH]) {
+  using TL = Tile<T, D>;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    s[nt] = f32x16{};
+    if constexpr (TL::F32) {
+#pragma unroll
+      for (int ks = 0; ks < TL::QK_STEPS; ++ks)
+        s[nt] = mfma_f32(__uint_as_float(b.k[ks >> 2][ks & 3]), __uint_as_float(q[nt][ks >> 2][ks & 3]), s[nt]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < TL::QK_STEPS; ++ks) s[nt] = mfma_bf16(as_bf16x8(b.k[ks]), as_bf16x8(q[nt][ks]), s[nt]);
+    }
+  }
+}
+
+// Masking of entries past the key count and the online softmax update; leaves
+// the step's probabilities exp2(s*c - m) in s.
+template <typename T, int D, bool PV>
+__device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], int t0, int nkeys, float c, int hf) {
+  using TL = Tile<T, D>;
+  if (t0 + 32 > nkeys) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (t0 + 16 * hf + r >= nkeys) s[nt][r] = -INFINITY;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float mx = s[nt][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+    mx = pair_max(mx) * c;
+    // Lazy rescaling: the offset only moves when the maximum grows by more than
+    // 2^8, so probabilities stay below 256 and the rescale of O is rare.
+    const bool need = mx > st.m[nt] + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? mx : st.m[nt];
+      const float alpha = need ? fast_exp2(st.m[nt] - mnew) : 1.0f;
+      st.l[nt] *= alpha;
+      st.m[nt] = mnew;
+      if constexpr (PV) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float ar = lane_read(alpha, 8 * (r >> 2) + 4 * hf + (r & 3));
+#pragma unroll
+          for (int cc = 0; cc < TL::VEC; ++cc) st.o[nt][cc][r] *= ar;
+        }
+      }
+    }
+    const float moff = st.m[nt] == -INFINITY ? 0.0f : st.m[nt];
+    float ls = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[nt][r] = fast_exp2(__builtin_fmaf(s[nt][r], c, -moff));
+      ls += s[nt][r];
+    }
+    st.l[nt] += ls;
+  }
+}
+
+// O += P * V_step.
+template <typename T, int D, bool PV>
+__device__ __forceinline__ void pv(State<T, D, PV>& st, const f32x16 (&p)[2], const KV<T, D>& b) {
+  using TL = Tile<T, D>;
+  if constexpr (TL::F32) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+        for (int cc = 0; cc < TL::VEC; ++cc)
+          st.o[nt][cc] = mfma_f32(p[nt][kk], __uint_as_float(b.v[kk].w[cc]), st.o[nt][cc]);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pa[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[nt][8 * ks + 2 * i], p[nt][8 * ks + 2 * i + 1]);
+        pa[nt] = as_bf16x8(w);
+      }
+#pragma unroll
+      for (int cc = 0; cc < TL::VEC; ++cc) {
+        const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = __builtin_amdgcn_perm(vword(b.v[8 * ks + 2 * i + 1], cc), vword(b.v[8 * ks + 2 * i], cc), sel);
+        const bf16x8 vb = as_bf16x8(w);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) st.o[nt][cc] = mfma_bf16(pa[nt], vb, st.o[nt][cc]);
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool GATHER, int EPI, bool PV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_kernel(AttnArgs a) {
+  using TL = Tile<T, D>;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int hf = lane >> 5, lm = lane & 31;
+  const int items = a.H * a.G;
+  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2);
+  if (blk < 0) return;
+  const int item = blk * 4 + wid;
+  if (item >= items) return;  // no block-level synchronisation below
+  const int h = item / a.G, g = item - h * a.G;
+  const int N = a.N;
+  const size_t head_off = (size_t)h * N * TL::ROWB;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * TL::ROWB);
+  const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
+  const auto rk = make_rsrc((const char*)a.k + head_off, head_bytes);
+  const auto rv = make_rsrc((const char*)a.v + head_off, head_bytes);
+  const int nkeys = a.nkeys;
+  const auto ridx = GATHER ? make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad, (uint32_t)a.kpad * 4u)
+                           : make_rsrc(nullptr, 0);
+
+  // This lane's two query columns (queries lm and lm + 32 of the group).
+  int tokq[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int slot = g * 64 + lm + 32 * nt;
+    qvalid[nt] = slot < N;
+    tokq[nt] = qvalid[nt] ? (a.perm ? a.perm[(size_t)h * N + slot] : slot) : 0;
+  }
+  u32x4 q[2][TL::KCH];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
+#pragma unroll
+    for (int c = 0; c < TL::KCH; ++c) q[nt][c] = bload128(rq, qb + c * TL::KSTRIDE);
+  }
+
+  State<T, D, PV> st;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    st.m[nt] = -INFINITY;
+    st.l[nt] = 0.0f;
+    if constexpr (PV) {
+#pragma unroll
+      for (int cc = 0; cc < TL::VEC; ++cc) st.o[nt][cc] = f32x16{};
+    }
+  }
+
+  // Software pipeline with one K/V buffer: the next step's K rows are requested as
+  // soon as this step's S^T has consumed the K registers, its V rows as soon as
+  // the PV product has consumed the V registers, and the indices of the step
+  // after that right behind them.
+  Idx ix;
+  KV<T, D> b;
+  const int nsteps = (nkeys + 31) >> 5;
+  load_idx<GATHER>(ix, ridx, 0, nkeys, lm, hf);
+  load_k<T, D>(b, ix, rk, hf);
+  if constexpr (PV) load_v<T, D>(b, ix, rv, lm);
+  if (nsteps > 1) load_idx<GATHER>(ix, ridx, 32, nkeys, lm, hf);
+  for (int it = 0; it < nsteps; ++it) {
+    const bool more = it + 1 < nsteps;
+    f32x16 s[2];
+    qk<T, D>(s, b, q);
+    if (more) load_k<T, D>(b, ix, rk, hf);
+    softmax<T, D, PV>(st, s, it * 32, nkeys, a.c, hf);
+    if constexpr (PV) {
+      pv<T, D, PV>(st, s, b);
+      if (more) load_v<T, D>(b, ix, rv, lm);
+    }
+    if (it + 2 < nsteps) load_idx<GATHER>(ix, ridx, (it + 2) * 32, nkeys, lm, hf);
+  }
+
+  // Row statistics: combine the two lane halves' partial sums.
+  float inv[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float lt = pair_sum(st.l[nt]);
+    inv[nt] = 1.0f / lt;
+    if (hf == 0 && qvalid[nt]) {
+      const size_t ri = (size_t)h * N + tokq[nt];
+      if (a.stats) a.stats[ri] = make_float2(st.m[nt], inv[nt]);
+      if (a.lse) a.lse[ri] = (st.m[nt] + __log2f(lt)) * kLn2;
+    }
+  }
+  if constexpr (PV) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 8 * (r >> 2) + 4 * hf + (r & 3);  // query row within this nt half
+        const float ir = lane_read(inv[nt], qi);
+        const int tok = lane_read_i(tokq[nt], qi);
+        if (g * 64 + qi + 32 * nt >= N) continue;
+        const size_t base = ((size_t)h * N + tok) * D + (size_t)lm * TL::VEC;
+        float vals[TL::VEC];
+#pragma unroll
+        for (int cc = 0; cc < TL::VEC; ++cc) vals[cc] = st.o[nt][cc][r] * ir;
+        if constexpr (TL::F32) {
+          const float* rin = (const float*)a.rin;
+          float* out = (float*)a.o + base;
+#pragma unroll
+          for (int cc = 0; cc < TL::VEC; ++cc) {
+            float x = vals[cc];
+            if constexpr (EPI == EPI_ADD) x += rin[base + cc];
+            if constexpr (EPI == EPI_RESID) x = rin[base + cc] - x;
+            out[cc] = x;
+          }
+        } else {
+          const __bf16* rin = (const __bf16*)a.rin;
+          if constexpr (EPI != EPI_PLAIN) {
+#pragma unroll
+            for (int cc = 0; cc < TL::VEC; ++cc) {
+              const float rv2 = (float)rin[base + cc];
+              vals[cc] = EPI == EPI_ADD ? vals[cc] + rv2 : rv2 - vals[cc];
+            }
+          }
+          uint32_t w[TL::VEC / 2];
+#pragma unroll
+          for (int i = 0; i < TL::VEC / 2; ++i) w[i] = pack_bf16x2(vals[2 * i], vals[2 * i + 1]);
+          uint32_t* out = (uint32_t*)((__bf16*)a.o + base);
+#pragma unroll
+          for (int i = 0; i < TL::VEC / 2; ++i) out[i] = w[i];
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool GATHER, int EPI, bool PV>
+hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  const int items = a.H * a.G;
+  const int blocks = xcd_grid((items + 3) / 4);
+  hipLaunchKernelGGL((attn_kernel<T, D, GATHER, EPI, PV>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const AttnArgs& a, bool gather, int epi, bool pv, hipStream_t s) {
+  if (!pv) return gather ? launch_t<T, D, true, EPI_PLAIN, false>(a, s) : launch_t<T, D, false, EPI_PLAIN, false>(a, s);
+  if (gather) {
+    switch (epi) {
+      case EPI_ADD: return launch_t<T, D, true, EPI_ADD, true>(a, s);
+      case EPI_RESID: return launch_t<T, D, true, EPI_RESID, true>(a, s);
+      default: return launch_t<T, D, true, EPI_PLAIN, true>(a, s);
+    }
+  }
+  return launch_t<T, D, false, EPI_PLAIN, true>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, bool gather, int epi, bool pv,
+                            hipStream_t s) {
+  if (dtype == DT_BF16) {
+    return head_dim == 128 ? launch_d<__bf16, 128>(a, gather, epi, pv, s) : launch_d<__bf16, 64>(a, gather, epi, pv, s);
+  }
+  return head_dim == 128 ? launch_d<float, 128>(a, gather, epi, pv, s) : launch_d<float, 64>(a, gather, epi, pv, s);
+}
+
+}  // namespace mcs

@@ -1,0 +1,61 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mcs {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { EPI_PLAIN = 0, EPI_ADD = 1, EPI_RESID = 2 };
+
+// Attention over query groups of 64 (one wavefront each).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* perm;  // [H][N] slot -> token, or null (slot == token)
+  const int32_t* idx;   // [H][G][kpad] kept keys of each group, or null (all N keys)
+  const void* rin;      // EPI_ADD: cached residual; EPI_RESID: dense output
+  void* o;              // [H][N][D] output (token order)
+  float2* stats;        // optional [H][N] {offset m (log2 units), 1 / sum exp2(s*c - m)}
+  float* lse;           // optional [H][N] natural-log logsumexp of scale * q.k
+  int H, N, G, nkeys, kpad;
+  float c;              // scale * log2(e)
+};
+hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, bool gather, int epi, bool pv,
+                            hipStream_t s);
+
+// Selection pass 2: summed normalised probabilities of every key per query group.
+struct MassArgs {
+  const void* q;
+  const void* k;
+  const int32_t* perm;     // [H][N]
+  const float2* stats;     // [H][N] row statistics from pass 1 (or null: use lse)
+  const float* lse;        // [H][N] natural-log logsumexp (used when stats is null)
+  float* mass;             // [hcount][G][N]
+  int h0, hcount, N, G;
+  float c;                 // scale * log2(e)
+};
+hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s);
+
+// Per-row exact top-K of non-negative fp32 masses, ascending key ids, -1 padded.
+struct TopkArgs {
+  const float* mass;  // [rows][N]
+  int32_t* idx;       // [rows][kpad]
+  int rows, N, K, kpad;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// PDDP grouping.
+struct PddpArgs {
+  const void* q;        // [H][N][D]
+  int32_t* perm;        // [H][N] output
+  void* ws;             // workspace (see pddp_workspace_bytes)
+  int H, N, D, C, iters;
+};
+size_t pddp_workspace_bytes(int H, int N, int D, int C);
+hipError_t launch_pddp(const PddpArgs& a, int dtype, hipStream_t s);
+
+}  // namespace mcs

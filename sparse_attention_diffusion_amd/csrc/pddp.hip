@@ -1,0 +1,527 @@
+// PDDP query grouping of the MC-Sparse hot path for gfx950 (MC-Sparse summary
+// page, grouping paragraph: project a node's queries onto its principal
+// direction, cut at the median, repeat until every group holds exactly C).
+//
+// The split tree's shape depends only on N and C (a node of n queries holds
+// g = ceil(n/C) groups and its left child takes floor(g/2)*C of them), so every
+// node is a contiguous slot range of perm known before any data is seen, and
+// node k of level l is found by walking the l bits of k from the root.  The
+// tree is processed one level at a time, all heads and all nodes of the level
+// in one launch per stage:
+//   1. stats   : per node, shifted sums  s = sum(x - r),  S = sum (x - r)(x - r)^T
+//                with r the node's first query (exact zero for identical queries,
+//                and no large-mean cancellation); S on v_mfma_f32_32x32x2_f32.
+//                Big nodes are split over several blocks that write partials.
+//   2. power   : mean mu = r + s/n, covariance  C = S - n*m*m^T  (m = s/n), then a
+//                fixed number of power steps from ones/sqrt(D) (stop only if
+//                |C v| = 0); fused into stage 1 when one block holds the node.
+//   3. project : p = (x - mu) . v for every slot, as an order-preserving uint32.
+//   4. split   : per node, radix select of the rank-cut element of the 64-bit
+//                composite (projection key, token id), then a stable partition of
+//                the node's slots: smaller composites to the left child.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mcs {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxParts = 64;  // blocks per node at the top levels
+constexpr int kTileRows = 32;  // rows staged in LDS per stats iteration
+
+struct Node {
+  int start, n;
+  bool internal;
+};
+
+__host__ __device__ inline Node walk_node(int N, int C, int level, int k) {
+  Node nd{0, N, false};
+  for (int d = 0; d < level; ++d) {
+    const int g = (nd.n + C - 1) / C;
+    if (g <= 1) return Node{0, 0, false};
+    const int cut = (g / 2) * C;
+    if ((k >> (level - 1 - d)) & 1) {
+      nd.start += cut;
+      nd.n -= cut;
+    } else {
+      nd.n = cut;
+    }
+  }
+  nd.internal = (nd.n + C - 1) / C >= 2;
+  return nd;
+}
+
+struct Level {
+  int level, nodes, parts;
+};
+
+// Workspace carve-up (all offsets 256-byte aligned).
+struct Ws {
+  int32_t* tmp_perm;   // [H][N]
+  uint32_t* keys;      // [H][N]
+  float* partials;     // [H][kMaxParts][D + D*D]
+  float* node_param;   // [H][max_nodes][2*D]   (mu, v)
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int level_count(int N, int C) {
+  const int G = (N + C - 1) / C;
+  int L = 0;
+  while ((1 << L) < G) ++L;  // ceil(log2 G)
+  return L;
+}
+
+inline int max_nodes(int N, int C) {
+  const int L = level_count(N, C);
+  return L == 0 ? 1 : (1 << (L - 1));
+}
+
+inline int parts_for(int N, int level) {
+  int p = (N >> level) / 1024;
+  return p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p);
+}
+
+inline Ws carve(void* base, int H, int N, int D, int C) {
+  char* p = (char*)base;
+  Ws w;
+  w.tmp_perm = (int32_t*)p;
+  p += align256((size_t)H * N * 4);
+  w.keys = (uint32_t*)p;
+  p += align256((size_t)H * N * 4);
+  w.partials = (float*)p;
+  p += align256((size_t)H * kMaxParts * (D + (size_t)D * D) * 4);
+  w.node_param = (float*)p;
+  return w;
+}
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p) { return (float)*p; }
+
+// Shared body of the stats kernel: accumulate the shifted sums of rows
+// [r0, r1) of a node into (colsum, acc tiles).  Rows are staged in LDS as fp32.
+template <typename T, int D>
+struct StatsAcc {
+  static constexpr int NT = D / 32;              // 32-wide tiles per dimension
+  static constexpr int TPW = NT * NT / 4;        // output tiles per wave
+  static constexpr int LDX = D + 32;             // padded LDS row stride (floats)
+  f32x16 acc[TPW];
+};
+
+template <typename T, int D>
+__device__ void stats_rows(const T* qh, const int32_t* permh, const float* ref, int r0, int r1, float* xs,
+                           StatsAcc<T, D>& sa, float& colsum) {
+  using SA = StatsAcc<T, D>;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hf = lane >> 5, lm = lane & 31;
+  for (int t = 0; t < SA::TPW; ++t) sa.acc[t] = f32x16{};
+  colsum = 0.0f;
+  for (int base = r0; base < r1; base += kTileRows) {
+    const int nrows = min(kTileRows, r1 - base);
+    __syncthreads();
+    for (int e = tid; e < kTileRows * D; e += kThreads) {
+      const int rr = e / D, d = e - rr * D;
+      float x = 0.0f;
+      if (rr < nrows) {
+        const int tok = permh[base + rr];
+        x = ldf(qh + (size_t)tok * D + d) - ref[d];
+      }
+      xs[rr * SA::LDX + d] = x;
+    }
+    __syncthreads();
+    if (tid < D) {
+      for (int rr = 0; rr < nrows; ++rr) colsum += xs[rr * SA::LDX + tid];
+    }
+    // S += X^T X over this tile: k-step s covers rows 2s, 2s+1 (k = half of the wave).
+    for (int s = 0; s < kTileRows / 2; ++s) {
+      const float* row = xs + (2 * s + hf) * SA::LDX;
+      if constexpr (D == 128) {
+        const float a = row[lm + 32 * wid];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) sa.acc[tb] = mfma_f32(a, row[lm + 32 * tb], sa.acc[tb]);
+      } else {
+        const int ta = wid >> 1, tb = wid & 1;
+        sa.acc[0] = mfma_f32(row[lm + 32 * ta], row[lm + 32 * tb], sa.acc[0]);
+      }
+    }
+  }
+}
+
+// Write the accumulated S tiles into a row-major D x D destination (LDS or global).
+template <typename T, int D>
+__device__ void store_tiles(const StatsAcc<T, D>& sa, float* dst) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, hf = lane >> 5, lm = lane & 31;
+#pragma unroll
+  for (int t = 0; t < StatsAcc<T, D>::TPW; ++t) {
+    const int ta = D == 128 ? wid : (wid >> 1);
+    const int tb = D == 128 ? t : (wid & 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int b = 32 * tb + lm;
+      dst[a * D + b] = sa.acc[t][r];
+    }
+  }
+}
+
+// Power iteration on the centred covariance held in LDS; writes mu and v.
+template <int D>
+__device__ void power_and_store(float* cov, const float* m_shift, const float* ref, int n, int iters, float* vbuf,
+                                float* red, float* out_param) {
+  const int tid = threadIdx.x;
+  // centre: C = S - n m m^T
+  for (int e = tid; e < D * D; e += kThreads) {
+    const int a = e / D, b = e - a * D;
+    cov[e] -= (float)n * m_shift[a] * m_shift[b];
+  }
+  if (tid < D) vbuf[tid] = 1.0f / sqrtf((float)D);
+  __syncthreads();
+  constexpr int TPR = kThreads / D;  // threads per row of the mat-vec
+  const int a = tid / TPR, part = tid % TPR;
+  for (int it = 0; it < iters; ++it) {
+    float w = 0.0f;
+    for (int b = part; b < D; b += TPR) w = __builtin_fmaf(cov[a * D + b], vbuf[b], w);
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) w += __shfl_xor(w, o, 64);
+    float sq = (part == 0) ? w * w : 0.0f;
+    sq = wave_sum(sq);
+    if ((tid & 63) == 0) red[tid >> 6] = sq;
+    __syncthreads();
+    const float nrm2 = red[0] + red[1] + red[2] + red[3];
+    if (nrm2 == 0.0f) break;  // uniform: every thread read the same sum
+    const float inv = 1.0f / sqrtf(nrm2);
+    __syncthreads();
+    if (part == 0) vbuf[a] = w * inv;
+    __syncthreads();
+  }
+  __syncthreads();
+  if (tid < D) {
+    out_param[tid] = ref[tid] + m_shift[tid];  // mu
+    out_param[D + tid] = vbuf[tid];            // v
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pddp_stats_kernel(PddpArgs a, Ws w, Level lv) {
+  extern __shared__ float smem[];
+  using SA = StatsAcc<T, D>;
+  const int P = lv.parts;
+  const int per_head = lv.nodes * P;
+  const int h = blockIdx.x / per_head;
+  const int rem = blockIdx.x - h * per_head;
+  const int k = rem / P, part = rem - k * P;
+  const Node nd = walk_node(a.N, a.C, lv.level, k);
+  if (!nd.internal) return;
+  const int chunk = (nd.n + P - 1) / P;
+  const int r0 = nd.start + part * chunk;
+  const int r1 = min(nd.start + nd.n, r0 + chunk);
+  const T* qh = (const T*)a.q + (size_t)h * a.N * D;
+  const int32_t* permh = a.perm + (size_t)h * a.N;
+
+  float* xs = smem;                          // kTileRows * LDX
+  float* ref = xs + kTileRows * SA::LDX;     // D
+  float* msh = ref + D;                      // D
+  float* vbuf = msh + D;                     // D
+  float* red = vbuf + D;                     // 8
+  float* cov = red + 8;                      // D*D (fused only)
+  const int tid = threadIdx.x;
+  const int tok0 = permh[nd.start];
+  if (tid < D) ref[tid] = ldf(qh + (size_t)tok0 * D + tid);
+  __syncthreads();
+  SA sa;
+  float colsum;
+  stats_rows<T, D>(qh, permh, ref, max(r0, nd.start), max(r1, r0), xs, sa, colsum);
+  if (P > 1) {
+    float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)k * P + part) * (D + (size_t)D * D);
+    if (tid < D) dst[tid] = colsum;
+    store_tiles<T, D>(sa, dst + D);
+    return;
+  }
+  __syncthreads();
+  store_tiles<T, D>(sa, cov);
+  if (tid < D) msh[tid] = colsum / (float)nd.n;
+  __syncthreads();
+  const int maxn = 1 << lv.level;
+  power_and_store<D>(cov, msh, ref, nd.n, a.iters, vbuf, red,
+                     w.node_param + ((size_t)h * maxn + k) * 2 * D);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, Level lv) {
+  extern __shared__ float smem[];
+  const int h = blockIdx.x / lv.nodes;
+  const int k = blockIdx.x - h * lv.nodes;
+  const Node nd = walk_node(a.N, a.C, lv.level, k);
+  if (!nd.internal) return;
+  const int P = lv.parts;
+  const T* qh = (const T*)a.q + (size_t)h * a.N * D;
+  const int32_t* permh = a.perm + (size_t)h * a.N;
+  float* cov = smem;         // D*D
+  float* ref = cov + D * D;  // D
+  float* msh = ref + D;      // D
+  float* vbuf = msh + D;     // D
+  float* red = vbuf + D;     // 8
+  const int tid = threadIdx.x;
+  const float* src = w.partials + ((size_t)h * kMaxParts + (size_t)k * P) * (D + (size_t)D * D);
+  const size_t stride = D + (size_t)D * D;
+  for (int e = tid; e < D + D * D; e += kThreads) {
+    float s = 0.0f;
+    for (int p = 0; p < P; ++p) s += src[p * stride + e];  // fixed order: deterministic
+    if (e < D)
+      msh[e] = s / (float)nd.n;
+    else
+      cov[e - D] = s;
+  }
+  if (tid < D) ref[tid] = ldf(qh + (size_t)permh[nd.start] * D + tid);
+  __syncthreads();
+  const int maxn = 1 << lv.level;
+  power_and_store<D>(cov, msh, ref, nd.n, a.iters, vbuf, red, w.node_param + ((size_t)h * maxn + k) * 2 * D);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pddp_project_kernel(PddpArgs a, Ws w, Level lv) {
+  const int P = lv.parts;
+  const int per_head = lv.nodes * P;
+  const int h = blockIdx.x / per_head;
+  const int rem = blockIdx.x - h * per_head;
+  const int k = rem / P, part = rem - k * P;
+  const Node nd = walk_node(a.N, a.C, lv.level, k);
+  if (!nd.internal) return;
+  const int chunk = (nd.n + P - 1) / P;
+  const int r0 = nd.start + part * chunk;
+  const int r1 = min(nd.start + nd.n, r0 + chunk);
+  const int maxn = 1 << lv.level;
+  const float* prm = w.node_param + ((size_t)h * maxn + k) * 2 * D;
+  const T* qh = (const T*)a.q + (size_t)h * a.N * D;
+  const int32_t* permh = a.perm + (size_t)h * a.N;
+  uint32_t* keys = w.keys + (size_t)h * a.N;
+  // 16 lanes per row, D/16 dims per lane.
+  constexpr int DPL = D / 16;
+  const int tid = threadIdx.x, sub = tid & 15, rgrp = tid >> 4;
+  float mu[DPL], v[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
+    mu[j] = prm[sub * DPL + j];
+    v[j] = prm[D + sub * DPL + j];
+  }
+  for (int row = r0 + rgrp; row < r1; row += kThreads / 16) {
+    const int tok = permh[row];
+    const T* x = qh + (size_t)tok * D + sub * DPL;
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(ldf(x + j) - mu[j], v[j], p);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
+    if (sub == 0) keys[row] = float_key(p);
+  }
+}
+
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t d) {
+  uint64_t todo = __builtin_amdgcn_ballot_w64(active);
+  while (todo) {
+    const int leader = __builtin_ctzll(todo);
+    const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+    const uint64_t same = __builtin_amdgcn_ballot_w64(active && d == ld);
+    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[ld], (uint32_t)__builtin_popcountll(same));
+    todo &= ~same;
+  }
+}
+
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& incl) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum[wid] = v;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int ww = 0; ww < kThreads / 64; ++ww) {
+    const uint32_t t = wsum[ww];
+    if (ww < wid) before += t;
+    total += t;
+  }
+  __syncthreads();
+  incl = v + before;
+  return total;
+}
+
+// One radix pass over the node: histogram of digit `shift` of the selected word
+// among entries whose already-fixed bits match; returns the digit holding rank kr
+// (0-based, ascending) and updates kr to the rank inside that digit.
+__device__ uint32_t radix_pass(const uint32_t* keys, const int32_t* toks, int start, int n, bool use_tok,
+                               uint32_t hi_val, uint32_t prefix, uint32_t pmask, int shift, uint32_t& kr,
+                               uint32_t* hist, uint32_t* bcast) {
+  const int tid = threadIdx.x;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int b = 0; b < n; b += kThreads) {
+    const int i = b + tid;
+    bool act = i < n;
+    uint32_t word = 0;
+    if (act) {
+      const uint32_t hk = keys[start + i];
+      if (use_tok) {
+        act = hk == hi_val;
+        word = (uint32_t)toks[start + i];
+      } else {
+        word = hk;
+      }
+      act = act && (word & pmask) == prefix;
+    }
+    hist_add(hist, act, (word >> shift) & 255u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t below = 0;
+    int d = 0;
+    for (; d < 255; ++d) {
+      if (below + hist[d] > kr) break;
+      below += hist[d];
+    }
+    bcast[0] = (uint32_t)d;
+    bcast[1] = kr - below;
+  }
+  __syncthreads();
+  const uint32_t d = bcast[0];
+  kr = bcast[1];
+  __syncthreads();
+  return d;
+}
+
+__global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, Level lv) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[kThreads / 64];
+  __shared__ uint32_t bcast[2];
+  const int h = blockIdx.x / lv.nodes;
+  const int k = blockIdx.x - h * lv.nodes;
+  const Node nd = walk_node(a.N, a.C, lv.level, k);
+  if (!nd.internal) return;
+  const int g = (nd.n + a.C - 1) / a.C;
+  const uint32_t cut = (uint32_t)((g / 2) * a.C);
+  const uint32_t* keys = w.keys + (size_t)h * a.N;
+  const int32_t* src = w.tmp_perm + (size_t)h * a.N;  // this level's input order
+  int32_t* dst = a.perm + (size_t)h * a.N;
+
+  // Rank-cut element of the composite (key, token) in ascending order.
+  uint32_t kr = cut, prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    const uint32_t d = radix_pass(keys, src, nd.start, nd.n, false, 0, prefix, pmask, shift, kr, hist, bcast);
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+  }
+  const uint32_t thi = prefix;
+  uint32_t ttok = 0;
+  const bool need_tok = kr > 0;  // some entries equal to thi go left: split them by token id
+  if (need_tok) {
+    prefix = 0;
+    pmask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t d = radix_pass(keys, src, nd.start, nd.n, true, thi, prefix, pmask, shift, kr, hist, bcast);
+      prefix |= d << shift;
+      pmask |= 255u << shift;
+    }
+    ttok = prefix;
+  }
+
+  // Stable partition of the node's slots.
+  constexpr int E = 8;
+  const int tid = threadIdx.x;
+  uint32_t left_done = 0, right_done = 0;
+  for (int b = 0; b < nd.n; b += kThreads * E) {
+    const int i0 = b + tid * E;
+    int32_t tk[E];
+    bool lf[E];
+    uint32_t nl = 0, nr = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e;
+      lf[e] = false;
+      tk[e] = 0;
+      if (i < nd.n) {
+        const uint32_t hk = keys[nd.start + i];
+        tk[e] = src[nd.start + i];
+        lf[e] = hk < thi || (need_tok && hk == thi && (uint32_t)tk[e] < ttok);
+        nl += lf[e] ? 1u : 0u;
+        nr += lf[e] ? 0u : 1u;
+      }
+    }
+    uint32_t incl;
+    const uint32_t packed = nl | (nr << 16);
+    const uint32_t tot = block_scan(packed, wsum, incl);
+    uint32_t pl = left_done + (incl & 0xffffu) - nl;
+    uint32_t pr = right_done + (incl >> 16) - nr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (i0 + e >= nd.n) continue;
+      if (lf[e])
+        dst[nd.start + pl++] = tk[e];
+      else
+        dst[nd.start + cut + pr++] = tk[e];
+    }
+    left_done += tot & 0xffffu;
+    right_done += tot >> 16;
+  }
+}
+
+__global__ void iota_kernel(int32_t* perm, int H, int N) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (size_t)H * N) perm[i] = (int32_t)(i % (size_t)N);
+}
+
+template <typename T, int D>
+hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
+  Ws w = carve(a.ws, a.H, a.N, D, a.C);
+  const size_t total = (size_t)a.H * a.N;
+  hipLaunchKernelGGL(iota_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.perm, a.H, a.N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int L = level_count(a.N, a.C);
+  using SA = StatsAcc<T, D>;
+  const size_t stats_lds = (kTileRows * SA::LDX + 3 * D + 8) * sizeof(float);
+  const size_t fused_lds = stats_lds + (size_t)D * D * sizeof(float);
+  const size_t power_lds = ((size_t)D * D + 3 * D + 8) * sizeof(float);
+  // The fused stats kernel and the power kernel hold a D x D covariance in LDS
+  // (64 KiB at D = 128), above the default dynamic-LDS limit.
+  if ((e = hipFuncSetAttribute((const void*)pddp_stats_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)fused_lds)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute((const void*)pddp_power_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)power_lds)) != hipSuccess)
+    return e;
+  for (int l = 0; l < L; ++l) {
+    Level lv{l, 1 << l, parts_for(a.N, l)};
+    const unsigned nb = (unsigned)(a.H * lv.nodes * lv.parts);
+    if (lv.parts > 1) {
+      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), stats_lds, s, a, w, lv);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), power_lds, s, a, w, lv);
+    } else {
+      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), fused_lds, s, a, w, lv);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((pddp_project_kernel<T, D>), dim3(nb), dim3(kThreads), 0, s, a, w, lv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(w.tmp_perm, a.perm, total * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(pddp_split_kernel, dim3(a.H * lv.nodes), dim3(kThreads), 0, s, a, w, lv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t pddp_workspace_bytes(int H, int N, int D, int C) {
+  return align256((size_t)H * N * 4) * 2 + align256((size_t)H * kMaxParts * (D + (size_t)D * D) * 4) +
+         align256((size_t)H * max_nodes(N, C) * 2 * D * 4);
+}
+
+hipError_t launch_pddp(const PddpArgs& a, int dtype, hipStream_t s) {
+  if (dtype == DT_BF16) return a.D == 128 ? run_levels<__bf16, 128>(a, s) : run_levels<__bf16, 64>(a, s);
+  return a.D == 128 ? run_levels<float, 128>(a, s) : run_levels<float, 64>(a, s);
+}
+
+}  // namespace mcs

@@ -26,3 +26,11 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name the case before any GPU work so a fault that ends the process is attributable.
+    if "gpu" in request.keywords:
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield
