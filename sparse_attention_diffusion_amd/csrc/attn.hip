@@ -277,6 +277,10 @@ void attn_kernel(AttnArgs a) {
     const int slot = g * 64 + lm + 32 * nt;
     qvalid[nt] = slot < N;
     tokq[nt] = qvalid[nt] ? (a.perm ? a.perm[(size_t)h * N + slot] : slot) : 0;
+    if (tokq[nt] < 0 || tokq[nt] >= N) {  // not a token (corrupt perm): compute nothing for it
+      qvalid[nt] = false;
+      tokq[nt] = 0;
+    }
   }
   u32x4 q[2][TL::KCH];
 #pragma unroll
@@ -341,7 +345,8 @@ void attn_kernel(AttnArgs a) {
         const int qi = 8 * (r >> 2) + 4 * hf + (r & 3);  // query row within this nt half
         const float ir = lane_read(inv[nt], qi);
         const int tok = lane_read_i(tokq[nt], qi);
-        if (g * 64 + qi + 32 * nt >= N) continue;
+        const int ok = lane_read_i(qvalid[nt] ? 1 : 0, qi);
+        if (!ok) continue;  // padding slot of the last group, or an invalid perm entry
         const size_t base = ((size_t)h * N + tok) * D + (size_t)lm * TL::VEC;
         float vals[TL::VEC];
 #pragma unroll

@@ -78,9 +78,13 @@ inline int max_nodes(int N, int C) {
   return L == 0 ? 1 : (1 << (L - 1));
 }
 
+// Blocks per node: about one per 1024 rows, with at most kMaxParts partials per
+// head in total (nodes * parts <= kMaxParts); one block per node from level 6 on.
 inline int parts_for(int N, int level) {
   int p = (N >> level) / 1024;
-  return p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p);
+  const int cap = kMaxParts >> level;
+  if (p > cap) p = cap;
+  return p < 1 ? 1 : p;
 }
 
 inline Ws carve(void* base, int H, int N, int D, int C) {
@@ -457,10 +461,15 @@ __global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, 
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (i0 + e >= nd.n) continue;
-      if (lf[e])
-        dst[nd.start + pl++] = tk[e];
-      else
-        dst[nd.start + cut + pr++] = tk[e];
+      // the threshold puts exactly `cut` entries left; the bounds keep every
+      // store inside this node's slots regardless
+      if (lf[e]) {
+        if (pl < cut) dst[nd.start + pl] = tk[e];
+        ++pl;
+      } else {
+        if (pr < (uint32_t)nd.n - cut) dst[nd.start + cut + pr] = tk[e];
+        ++pr;
+      }
     }
     left_done += tot & 0xffffu;
     right_done += tot >> 16;

@@ -58,6 +58,10 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
     const int slot = g * 64 + lm + 32 * nt;
     qvalid[nt] = slot < N;
     tokq[nt] = qvalid[nt] ? a.perm[(size_t)h * N + slot] : 0;
+    if (tokq[nt] < 0 || tokq[nt] >= N) {  // not a token: treat as padding
+      qvalid[nt] = false;
+      tokq[nt] = 0;
+    }
     const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
 #pragma unroll
     for (int c = 0; c < TL::KCH; ++c) q[nt][c] = bload128(rq, qb + c * TL::KSTRIDE);
@@ -258,7 +262,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         keep = true;
         --eq_left;
       }
-      if (keep) out[pos++] = i0 + e;
+      if (keep) {
+        if (pos < (uint32_t)K) out[pos] = i0 + e;  // exactly K are kept; stay inside the row regardless
+        ++pos;
+      }
     }
     written += tot;
   }
