@@ -36,6 +36,12 @@ def assert_close(got, want, max_abs=MAX_ABS, mean_abs=MEAN_ABS, what=""):
     return mx, mn
 
 
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place at |x| (round-to-nearest error bound)."""
+    a = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 0.5 * np.exp2(np.floor(np.log2(a)) - 7)
+
+
 def check_index_row(row, mass, k, n):
     """GPU idx row vs the oracle's fp64 masses of that group (ties within TIE_REL)."""
     row = np.asarray(row)
