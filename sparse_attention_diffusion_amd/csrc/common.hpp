@@ -90,16 +90,22 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Map the
-// hardware block id so that XCD x runs the contiguous logical range
-// [x*per, (x+1)*per): neighbouring work items (adjacent query groups of one head,
-// which pick overlapping keys) then share an L2.  Returns -1 for padding blocks.
-__device__ __forceinline__ int xcd_remap(int hw_block, int n_logical) {
-  int per = (n_logical + kNumXcd - 1) / kNumXcd;
-  int logical = (hw_block % kNumXcd) * per + hw_block / kNumXcd;
-  return logical < n_logical ? logical : -1;
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own 4 MB L2), and
+// all XCDs share the MALL.  Map hardware block b (XCD b % 8, local slot b / 8) so
+// that each XCD runs `chunk` consecutive logical blocks at a time while the 8 XCDs
+// together sweep one window of 8*chunk consecutive blocks: neighbouring query
+// groups (which pick overlapping keys) share an L2, and the blocks in flight
+// across the chip stay within about one head's K/V (MALL-resident).  The last
+// partial window keeps the identity mapping.  Returns -1 for padding blocks.
+__device__ __forceinline__ int xcd_remap(int hw_block, int n_logical, int chunk) {
+  if (hw_block >= n_logical) return -1;
+  const int window = kNumXcd * chunk;
+  const int full = (n_logical / window) * window;
+  if (chunk <= 0 || hw_block >= full) return hw_block;
+  const int x = hw_block % kNumXcd, j = hw_block / kNumXcd;
+  return (j / chunk) * window + x * chunk + (j % chunk);
 }
-inline int xcd_grid(int n_logical) { return ((n_logical + kNumXcd - 1) / kNumXcd) * kNumXcd; }
+inline int xcd_grid(int n_logical) { return n_logical; }
 
 // Order-preserving map of a float onto uint32 (ascending floats -> ascending keys).
 __device__ __forceinline__ uint32_t float_key(float f) {

@@ -10,6 +10,10 @@ namespace mcs {
 enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { EPI_PLAIN = 0, EPI_ADD = 1, EPI_RESID = 2 };
 
+// Default blocks per XCD per scheduling window (see xcd_remap); overridable with
+// the MCS_XCD_CHUNK environment variable for tuning.
+int default_xcd_chunk();
+
 // Attention over query groups of 64 (one wavefront each).
 struct AttnArgs {
   const void* q;
@@ -23,6 +27,7 @@ struct AttnArgs {
   float* lse;           // optional [H][N] natural-log logsumexp of scale * q.k
   int H, N, G, nkeys, kpad;
   float c;              // scale * log2(e)
+  int xcd_chunk;        // blocks per XCD per window of the block-to-XCD mapping
 };
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, bool gather, int epi, bool pv,
                             hipStream_t s);
@@ -37,6 +42,7 @@ struct MassArgs {
   float* mass;             // [hcount][G][N]
   int h0, hcount, N, G;
   float c;                 // scale * log2(e)
+  int xcd_chunk;
 };
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s);
 

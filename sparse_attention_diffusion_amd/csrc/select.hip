@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int hf = lane >> 5, lm = lane & 31;
   const int items = a.hcount * a.G;
-  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2);
+  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
   if (blk < 0) return;
   const int item = blk * 4 + wid;
   if (item >= items) return;  // no block-level synchronisation below
