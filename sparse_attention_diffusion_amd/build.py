@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmcs.so")
 SOURCES = ["attn.hip", "select.hip", "pddp.hip", "api.cpp"]
+# Attention keeps its 64x128 fp32 output tile in VGPRs (MFMA accumulators in the
+# VGPR form), so the rare rescale of O needs no copies between register files.
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions stay off: the compiler emits only scalar fp32 VALU ops.
@@ -24,7 +27,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 def _compile(src: str) -> str:
     obj = os.path.join(OUT, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

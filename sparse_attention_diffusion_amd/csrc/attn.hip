@@ -90,30 +90,25 @@ __device__ __forceinline__ VRaw<VW> vload(__amdgpu_buffer_rsrc_t r, uint32_t off
   return x;
 }
 
+// Keys of the step's entries.  No clamping: an entry past K holds -1 (or lies past
+// kpad, where the index buffer reads as 0), and key * row_bytes of -1 wraps to an
+// offset past the end of the K/V buffers, which the buffer loads return as zeros;
+// those entries' scores are masked to -inf anyway.
 template <bool GATHER>
-__device__ __forceinline__ void load_idx(Idx& ix, __amdgpu_buffer_rsrc_t ridx, int t0, int nkeys, int lm, int hf) {
+__device__ __forceinline__ void load_idx(Idx& ix, __amdgpu_buffer_rsrc_t ridx, int t0, int lm, int hf) {
   if constexpr (GATHER) {
-    const int ek = t0 + a_row_entry(lm);
-    int kk = (int)bload32(ridx, (uint32_t)ek * 4u);
-    ix.k = (ek < nkeys && kk > 0) ? kk : 0;  // entries past K hold -1
+    ix.k = (int)bload32(ridx, (uint32_t)(t0 + a_row_entry(lm)) * 4u);
     const int ev = t0 + 16 * hf;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 w = bload128(ridx, (uint32_t)(ev + 4 * c) * 4u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int kv = (int)w[j];
-        ix.v[4 * c + j] = (ev + 4 * c + j < nkeys && kv > 0) ? kv : 0;
-      }
+      for (int j = 0; j < 4; ++j) ix.v[4 * c + j] = (int)w[j];
     }
   } else {
-    const int ek = t0 + a_row_entry(lm);
-    ix.k = ek < nkeys ? ek : 0;
+    ix.k = t0 + a_row_entry(lm);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      int e = t0 + 16 * hf + j;
-      ix.v[j] = e < nkeys ? e : 0;
-    }
+    for (int j = 0; j < 16; ++j) ix.v[j] = t0 + 16 * hf + j;
   }
 }
 
@@ -146,29 +141,51 @@ struct State {
 };
 
 // S^T of one 32-key step (rows: the step's keys, columns: the group's 64 queries).
+// The group's Q operands live in LDS in lane order: chunk (nt, c) of lane l at
+// ((nt * KCH + c) * 64 + l) * 16 bytes, so every read is one conflict-free
+// ds_read_b128 and Q costs no registers between steps.
+typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 template <typename T, int D>
-__device__ __forceinline__ void qk(f32x16 (&s)[2], const KV<T, D>& b, const u32x4 (&q)[2][Tile<T, D>::KCH]) {
+__device__ __forceinline__ u32x4 q_chunk(lds_u32x4* qs, int nt, int c) {
+  return qs[(nt * Tile<T, D>::KCH + c) * 64];
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void qk(f32x16 (&s)[2], const KV<T, D>& b, const u32x4* qs_base, int lane) {
   using TL = Tile<T, D>;
+  // The LDS address is made opaque on every step so the compiler neither forwards
+  // the staging stores nor hoists Q back into registers (which would push the
+  // loop into register spills); the reads themselves can still be batched.
+  uint32_t qa = (uint32_t)(uintptr_t)(qs_base + lane);
+  asm volatile("" : "+v"(qa));
+  lds_u32x4* qs = (lds_u32x4*)(uintptr_t)qa;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     s[nt] = f32x16{};
     if constexpr (TL::F32) {
 #pragma unroll
-      for (int ks = 0; ks < TL::QK_STEPS; ++ks)
-        s[nt] = mfma_f32(__uint_as_float(b.k[ks >> 2][ks & 3]), __uint_as_float(q[nt][ks >> 2][ks & 3]), s[nt]);
+      for (int c = 0; c < TL::KCH; ++c) {
+        const u32x4 qc = q_chunk<T, D>(qs, nt, c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          s[nt] = mfma_f32(__uint_as_float(b.k[c][j]), __uint_as_float(qc[j]), s[nt]);
+      }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < TL::QK_STEPS; ++ks) s[nt] = mfma_bf16(as_bf16x8(b.k[ks]), as_bf16x8(q[nt][ks]), s[nt]);
+      for (int ks = 0; ks < TL::QK_STEPS; ++ks)
+        s[nt] = mfma_bf16(as_bf16x8(b.k[ks]), as_bf16x8(q_chunk<T, D>(qs, nt, ks)), s[nt]);
     }
   }
 }
 
 // Masking of entries past the key count and the online softmax update; leaves
 // the step's probabilities exp2(s*c - m) in s.
-template <typename T, int D, bool PV>
-__device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], int t0, int nkeys, float c, int hf) {
+template <typename T, int D, bool PV, bool EXACT_SUM, bool MASK>
+__device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], uint32_t (&pk)[2][8], int t0, int nkeys,
+                                        float c, int hf) {
   using TL = Tile<T, D>;
-  if (t0 + 32 > nkeys) {
+  if constexpr (MASK) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -199,19 +216,35 @@ __device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], int
       }
     }
     const float moff = st.m[nt] == -INFINITY ? 0.0f : st.m[nt];
-    float ls = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[nt][r] = fast_exp2(__builtin_fmaf(s[nt][r], c, -moff));
-      ls += s[nt][r];
+    for (int r = 0; r < 16; ++r) s[nt][r] = fast_exp2(__builtin_fmaf(s[nt][r], c, -moff));
+    if constexpr (!TL::F32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[nt][i] = pack_bf16x2(s[nt][2 * i], s[nt][2 * i + 1]);
     }
-    st.l[nt] += ls;
+    if constexpr (EXACT_SUM || TL::F32) {
+      // fp32 row sums: the row statistics / logsumexp are consumed by selection
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls += s[nt][r];
+      st.l[nt] += ls;
+    } else {
+      // sum of the bf16-rounded probabilities that the PV product uses, so the
+      // normalisation matches the numerator (v_dot2_f32_bf16 against ones)
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      float ls = st.l[nt];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[nt][i]), one, ls, false);
+      st.l[nt] = ls;
+    }
   }
 }
 
 // O += P * V_step.
 template <typename T, int D, bool PV>
-__device__ __forceinline__ void pv(State<T, D, PV>& st, const f32x16 (&p)[2], const KV<T, D>& b) {
+__device__ __forceinline__ void pv(State<T, D, PV>& st, const f32x16 (&p)[2], const uint32_t (&pk)[2][8],
+                                   const KV<T, D>& b) {
   using TL = Tile<T, D>;
   if constexpr (TL::F32) {
 #pragma unroll
@@ -229,7 +262,7 @@ __device__ __forceinline__ void pv(State<T, D, PV>& st, const f32x16 (&p)[2], co
       for (int nt = 0; nt < 2; ++nt) {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[nt][8 * ks + 2 * i], p[nt][8 * ks + 2 * i + 1]);
+        for (int i = 0; i < 4; ++i) w[i] = pk[nt][4 * ks + i];
         pa[nt] = as_bf16x8(w);
       }
 #pragma unroll
@@ -251,7 +284,7 @@ template <typename T, int D, bool GATHER, int EPI, bool PV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnArgs a) {
   using TL = Tile<T, D>;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int hf = lane >> 5, lm = lane & 31;
   const int items = a.H * a.G;
   const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
@@ -282,12 +315,14 @@ void attn_kernel(AttnArgs a) {
       tokq[nt] = 0;
     }
   }
-  u32x4 q[2][TL::KCH];
+  // Stage this wave's Q operands in its LDS slice (written and read by this wave only).
+  __shared__ u32x4 q_lds[4][2 * TL::KCH * 64];
+  u32x4* qs = q_lds[wid];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
 #pragma unroll
-    for (int c = 0; c < TL::KCH; ++c) q[nt][c] = bload128(rq, qb + c * TL::KSTRIDE);
+    for (int c = 0; c < TL::KCH; ++c) qs[(nt * TL::KCH + c) * 64 + lane] = bload128(rq, qb + c * TL::KSTRIDE);
   }
 
   State<T, D, PV> st;
@@ -308,21 +343,30 @@ void attn_kernel(AttnArgs a) {
   Idx ix;
   KV<T, D> b;
   const int nsteps = (nkeys + 31) >> 5;
-  load_idx<GATHER>(ix, ridx, 0, nkeys, lm, hf);
+  load_idx<GATHER>(ix, ridx, 0, lm, hf);
   load_k<T, D>(b, ix, rk, hf);
   if constexpr (PV) load_v<T, D>(b, ix, rv, lm);
-  if (nsteps > 1) load_idx<GATHER>(ix, ridx, 32, nkeys, lm, hf);
-  for (int it = 0; it < nsteps; ++it) {
-    const bool more = it + 1 < nsteps;
+  load_idx<GATHER>(ix, ridx, 32, lm, hf);
+  // Steps before the last: no masking, no branches around the prefetches (reads
+  // past the key list return zeros or valid rows that are never used).
+  for (int it = 0; it + 1 < nsteps; ++it) {
     f32x16 s[2];
-    qk<T, D>(s, b, q);
-    if (more) load_k<T, D>(b, ix, rk, hf);
-    softmax<T, D, PV>(st, s, it * 32, nkeys, a.c, hf);
+    uint32_t pk[2][8];
+    qk<T, D>(s, b, qs, lane);
+    load_k<T, D>(b, ix, rk, hf);
+    softmax<T, D, PV, !GATHER, false>(st, s, pk, it * 32, nkeys, a.c, hf);
     if constexpr (PV) {
-      pv<T, D, PV>(st, s, b);
-      if (more) load_v<T, D>(b, ix, rv, lm);
+      pv<T, D, PV>(st, s, pk, b);
+      load_v<T, D>(b, ix, rv, lm);
     }
-    if (it + 2 < nsteps) load_idx<GATHER>(ix, ridx, (it + 2) * 32, nkeys, lm, hf);
+    load_idx<GATHER>(ix, ridx, (it + 2) * 32, lm, hf);
+  }
+  {
+    f32x16 s[2];
+    uint32_t pk[2][8];
+    qk<T, D>(s, b, qs, lane);
+    softmax<T, D, PV, !GATHER, true>(st, s, pk, (nsteps - 1) * 32, nkeys, a.c, hf);
+    if constexpr (PV) pv<T, D, PV>(st, s, pk, b);
   }
 
   // Row statistics: combine the two lane halves' partial sums.

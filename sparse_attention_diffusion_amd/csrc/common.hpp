@@ -46,6 +46,10 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Index of this wavefront in its workgroup, as a wave-uniform (scalar) value so
+// that everything derived from it (head, group, buffer descriptors) stays in SGPRs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Pack two floats into a dword of two bf16 (round to nearest even), lo first.

@@ -34,7 +34,7 @@ struct QTile {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   using TL = QTile<T, D>;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int hf = lane >> 5, lm = lane & 31;
   const int items = a.hcount * a.G;
   const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
