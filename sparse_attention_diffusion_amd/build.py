@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmcs.so")
 SOURCES = ["attn.hip", "select.hip", "pddp.hip", "api.cpp"]
 # Attention keeps its 64x128 fp32 output tile in VGPRs (MFMA accumulators in the
 # VGPR form), so the rare rescale of O needs no copies between register files.
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions stay off: the compiler emits only scalar fp32 VALU ops.

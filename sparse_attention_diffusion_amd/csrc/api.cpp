@@ -106,17 +106,11 @@ int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
     m.G = G;
     m.c = (float)((double)d->scale * 1.4426950408889634);
     m.xcd_chunk = mcs::default_xcd_chunk();
+    m.idx = idx;
+    m.K = d->topk;
+    m.kpad = d->kpad;
     hipError_t e = mcs::launch_group_mass(m, d->dtype, d->head_dim, s);
-    if (e != hipSuccess) return hip_fail(e, "group mass launch");
-    mcs::TopkArgs t{};
-    t.mass = mass;
-    t.idx = idx + (size_t)h0 * G * d->kpad;
-    t.rows = hc * G;
-    t.N = d->n;
-    t.K = d->topk;
-    t.kpad = d->kpad;
-    e = mcs::launch_topk(t, s);
-    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    if (e != hipSuccess) return hip_fail(e, "selection pass 2 launch");
   }
   return MCS_OK;
 }

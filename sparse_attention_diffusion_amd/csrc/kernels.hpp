@@ -32,27 +32,22 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, bool gather, int epi, bool pv,
                             hipStream_t s);
 
-// Selection pass 2: summed normalised probabilities of every key per query group.
+// Selection pass 2 with the per-group top-K fused into its epilogue: summed
+// normalised probabilities of every key per query group (written to `mass`),
+// then the K keys of largest mass per group, ascending, -1 padded to kpad.
 struct MassArgs {
   const void* q;
   const void* k;
   const int32_t* perm;     // [H][N]
   const float2* stats;     // [H][N] row statistics from pass 1 (or null: use lse)
   const float* lse;        // [H][N] natural-log logsumexp (used when stats is null)
-  float* mass;             // [hcount][G][N]
-  int h0, hcount, N, G;
+  float* mass;             // [hcount][G][N] scratch rows
+  int32_t* idx;            // [H][G][kpad] output
+  int h0, hcount, N, G, K, kpad;
   float c;                 // scale * log2(e)
   int xcd_chunk;
 };
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s);
-
-// Per-row exact top-K of non-negative fp32 masses, ascending key ids, -1 padded.
-struct TopkArgs {
-  const float* mass;  // [rows][N]
-  int32_t* idx;       // [rows][kpad]
-  int rows, N, K, kpad;
-};
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // PDDP grouping.
 struct PddpArgs {

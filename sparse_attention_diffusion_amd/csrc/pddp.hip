@@ -103,46 +103,83 @@ inline Ws carve(void* base, int H, int N, int D, int C) {
 template <typename T>
 __device__ __forceinline__ float ldf(const T* p) { return (float)*p; }
 
-// Shared body of the stats kernel: accumulate the shifted sums of rows
-// [r0, r1) of a node into (colsum, acc tiles).  Rows are staged in LDS as fp32.
+// Accumulated statistics of one block: fp32 MFMA tiles of S = sum (x - r)(x - r)^T.
+// D = 128: 4 x 4 tiles of 32 x 32, wave w owns tile row w; D = 64: 2 x 2, one per wave.
 template <typename T, int D>
 struct StatsAcc {
-  static constexpr int NT = D / 32;              // 32-wide tiles per dimension
-  static constexpr int TPW = NT * NT / 4;        // output tiles per wave
-  static constexpr int LDX = D + 32;             // padded LDS row stride (floats)
+  static constexpr int NT = D / 32;
+  static constexpr int TPW = NT * NT / 4;  // output tiles per wave
+  static constexpr int LDX = D + 32;       // padded LDS row stride (floats): rows 2s, 2s+1 hit disjoint banks
+  static constexpr int TILE_ROWS = 64;     // rows staged per iteration (32 MFMA k-steps)
+  static constexpr int CH = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per chunk
   f32x16 acc[TPW];
 };
 
+// Shared-memory footprint of the statistics kernels (floats): the row tile and the
+// covariance never live at the same time, so they share one region.
+template <typename T, int D>
+constexpr int stats_region_floats() {
+  using SA = StatsAcc<T, D>;
+  return SA::TILE_ROWS * SA::LDX > D * D ? SA::TILE_ROWS * SA::LDX : D * D;
+}
+
+template <typename T>
+__device__ __forceinline__ void chunk_to_f32(u32x4 w, float* out);
+template <>
+__device__ __forceinline__ void chunk_to_f32<__bf16>(u32x4 w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = bf16lo(w[i]);
+    out[2 * i + 1] = bf16hi(w[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void chunk_to_f32<float>(u32x4 w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+}
+
+// Accumulate the shifted sums of rows [r0, r1) of a node (slots, mapped through
+// perm) into colsum (threads tid < D own one column) and the MFMA tiles.
 template <typename T, int D>
 __device__ void stats_rows(const T* qh, const int32_t* permh, const float* ref, int r0, int r1, float* xs,
                            StatsAcc<T, D>& sa, float& colsum) {
   using SA = StatsAcc<T, D>;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hf = lane >> 5, lm = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
   for (int t = 0; t < SA::TPW; ++t) sa.acc[t] = f32x16{};
   colsum = 0.0f;
-  for (int base = r0; base < r1; base += kTileRows) {
-    const int nrows = min(kTileRows, r1 - base);
-    __syncthreads();
-    for (int e = tid; e < kTileRows * D; e += kThreads) {
-      const int rr = e / D, d = e - rr * D;
-      float x = 0.0f;
+  for (int base = r0; base < r1; base += SA::TILE_ROWS) {
+    const int nrows = min(SA::TILE_ROWS, r1 - base);
+    __syncthreads();  // previous tile fully consumed
+    for (int e = tid; e < SA::TILE_ROWS * SA::CH; e += kThreads) {
+      const int rr = e / SA::CH, ch = e - rr * SA::CH;
+      float x[SA::EPC];
       if (rr < nrows) {
         const int tok = permh[base + rr];
-        x = ldf(qh + (size_t)tok * D + d) - ref[d];
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qh + (size_t)tok * D + ch * SA::EPC);
+        chunk_to_f32<T>(w, x);
+#pragma unroll
+        for (int i = 0; i < SA::EPC; ++i) x[i] -= ref[ch * SA::EPC + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < SA::EPC; ++i) x[i] = 0.0f;
       }
-      xs[rr * SA::LDX + d] = x;
+#pragma unroll
+      for (int i = 0; i < SA::EPC; ++i) xs[rr * SA::LDX + ch * SA::EPC + i] = x[i];
     }
     __syncthreads();
     if (tid < D) {
       for (int rr = 0; rr < nrows; ++rr) colsum += xs[rr * SA::LDX + tid];
     }
-    // S += X^T X over this tile: k-step s covers rows 2s, 2s+1 (k = half of the wave).
-    for (int s = 0; s < kTileRows / 2; ++s) {
+    // S += X^T X: k-step s covers rows 2s (lanes 0-31) and 2s+1 (lanes 32-63).
+    const int ksteps = (nrows + 1) >> 1;
+    for (int s = 0; s < ksteps; ++s) {
       const float* row = xs + (2 * s + hf) * SA::LDX;
       if constexpr (D == 128) {
-        const float a = row[lm + 32 * wid];
+        const float av = row[lm + 32 * wid];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) sa.acc[tb] = mfma_f32(a, row[lm + 32 * tb], sa.acc[tb]);
+        for (int tb = 0; tb < 4; ++tb) sa.acc[tb] = mfma_f32(av, row[lm + 32 * tb], sa.acc[tb]);
       } else {
         const int ta = wid >> 1, tb = wid & 1;
         sa.acc[0] = mfma_f32(row[lm + 32 * ta], row[lm + 32 * tb], sa.acc[0]);
@@ -154,7 +191,7 @@ __device__ void stats_rows(const T* qh, const int32_t* permh, const float* ref, 
 // Write the accumulated S tiles into a row-major D x D destination (LDS or global).
 template <typename T, int D>
 __device__ void store_tiles(const StatsAcc<T, D>& sa, float* dst) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, hf = lane >> 5, lm = lane & 31;
+  const int lane = threadIdx.x & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
 #pragma unroll
   for (int t = 0; t < StatsAcc<T, D>::TPW; ++t) {
     const int ta = D == 128 ? wid : (wid >> 1);
@@ -169,33 +206,42 @@ __device__ void store_tiles(const StatsAcc<T, D>& sa, float* dst) {
 }
 
 // Power iteration on the centred covariance held in LDS; writes mu and v.
+// The covariance is symmetric, so w[a] = sum_b C[b][a] v[b] reads C by columns:
+// consecutive lanes touch consecutive addresses (no bank conflicts).
 template <int D>
 __device__ void power_and_store(float* cov, const float* m_shift, const float* ref, int n, int iters, float* vbuf,
                                 float* red, float* out_param) {
   const int tid = threadIdx.x;
-  // centre: C = S - n m m^T
   for (int e = tid; e < D * D; e += kThreads) {
     const int a = e / D, b = e - a * D;
     cov[e] -= (float)n * m_shift[a] * m_shift[b];
   }
   if (tid < D) vbuf[tid] = 1.0f / sqrtf((float)D);
   __syncthreads();
-  constexpr int TPR = kThreads / D;  // threads per row of the mat-vec
-  const int a = tid / TPR, part = tid % TPR;
+  constexpr int PARTS = kThreads / D;  // column partitions (2 at D = 128, 4 at D = 64)
+  constexpr int BPP = D / PARTS;
+  const int a = tid % D, part = tid / D;
+  float* wpart = red + 8;              // PARTS * D partial sums
   for (int it = 0; it < iters; ++it) {
     float w = 0.0f;
-    for (int b = part; b < D; b += TPR) w = __builtin_fmaf(cov[a * D + b], vbuf[b], w);
-#pragma unroll
-    for (int o = TPR / 2; o >= 1; o >>= 1) w += __shfl_xor(w, o, 64);
-    float sq = (part == 0) ? w * w : 0.0f;
+#pragma unroll 8
+    for (int j = 0; j < BPP; ++j) {
+      const int b = part * BPP + j;
+      w = __builtin_fmaf(cov[b * D + a], vbuf[b], w);
+    }
+    wpart[part * D + a] = w;
+    __syncthreads();
+    float wa = 0.0f, sq = 0.0f;
+    if (tid < D) {
+      for (int p = 0; p < PARTS; ++p) wa += wpart[p * D + tid];
+      sq = wa * wa;
+    }
     sq = wave_sum(sq);
     if ((tid & 63) == 0) red[tid >> 6] = sq;
     __syncthreads();
     const float nrm2 = red[0] + red[1] + red[2] + red[3];
     if (nrm2 == 0.0f) break;  // uniform: every thread read the same sum
-    const float inv = 1.0f / sqrtf(nrm2);
-    __syncthreads();
-    if (part == 0) vbuf[a] = w * inv;
+    if (tid < D) vbuf[tid] = wa * (1.0f / sqrtf(nrm2));
     __syncthreads();
   }
   __syncthreads();
@@ -222,31 +268,30 @@ __global__ __launch_bounds__(kThreads) void pddp_stats_kernel(PddpArgs a, Ws w, 
   const T* qh = (const T*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
 
-  float* xs = smem;                          // kTileRows * LDX
-  float* ref = xs + kTileRows * SA::LDX;     // D
-  float* msh = ref + D;                      // D
-  float* vbuf = msh + D;                     // D
-  float* red = vbuf + D;                     // 8
-  float* cov = red + 8;                      // D*D (fused only)
+  float* region = smem;                                 // row tile, later the covariance
+  float* ref = region + stats_region_floats<T, D>();    // D
+  float* msh = ref + D;                                 // D
+  float* vbuf = msh + D;                                // D
+  float* red = vbuf + D;                                // 8 + (threads / D) * D
   const int tid = threadIdx.x;
   const int tok0 = permh[nd.start];
   if (tid < D) ref[tid] = ldf(qh + (size_t)tok0 * D + tid);
   __syncthreads();
   SA sa;
   float colsum;
-  stats_rows<T, D>(qh, permh, ref, max(r0, nd.start), max(r1, r0), xs, sa, colsum);
+  stats_rows<T, D>(qh, permh, ref, r0, max(r1, r0), region, sa, colsum);
   if (P > 1) {
     float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)k * P + part) * (D + (size_t)D * D);
     if (tid < D) dst[tid] = colsum;
     store_tiles<T, D>(sa, dst + D);
     return;
   }
-  __syncthreads();
-  store_tiles<T, D>(sa, cov);
+  __syncthreads();  // all MFMA reads of the row tile are done before it becomes the covariance
+  store_tiles<T, D>(sa, region);
   if (tid < D) msh[tid] = colsum / (float)nd.n;
   __syncthreads();
   const int maxn = 1 << lv.level;
-  power_and_store<D>(cov, msh, ref, nd.n, a.iters, vbuf, red,
+  power_and_store<D>(region, msh, ref, nd.n, a.iters, vbuf, red,
                      w.node_param + ((size_t)h * maxn + k) * 2 * D);
 }
 
@@ -260,16 +305,17 @@ __global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, 
   const int P = lv.parts;
   const T* qh = (const T*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
-  float* cov = smem;         // D*D
-  float* ref = cov + D * D;  // D
-  float* msh = ref + D;      // D
-  float* vbuf = msh + D;     // D
-  float* red = vbuf + D;     // 8
+  float* cov = smem;                               // D*D
+  float* ref = cov + stats_region_floats<T, D>();  // D
+  float* msh = ref + D;                            // D
+  float* vbuf = msh + D;                           // D
+  float* red = vbuf + D;                           // 8 + (threads / D) * D
   const int tid = threadIdx.x;
   const float* src = w.partials + ((size_t)h * kMaxParts + (size_t)k * P) * (D + (size_t)D * D);
   const size_t stride = D + (size_t)D * D;
   for (int e = tid; e < D + D * D; e += kThreads) {
     float s = 0.0f;
+#pragma unroll 8
     for (int p = 0; p < P; ++p) s += src[p * stride + e];  // fixed order: deterministic
     if (e < D)
       msh[e] = s / (float)nd.n;
@@ -332,7 +378,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t d
 }
 
 __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& incl) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   uint32_t v = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -489,27 +535,24 @@ hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int L = level_count(a.N, a.C);
-  using SA = StatsAcc<T, D>;
-  const size_t stats_lds = (kTileRows * SA::LDX + 3 * D + 8) * sizeof(float);
-  const size_t fused_lds = stats_lds + (size_t)D * D * sizeof(float);
-  const size_t power_lds = ((size_t)D * D + 3 * D + 8) * sizeof(float);
-  // The fused stats kernel and the power kernel hold a D x D covariance in LDS
-  // (64 KiB at D = 128), above the default dynamic-LDS limit.
+  const size_t lds = (size_t)(stats_region_floats<T, D>() + 3 * D + 8 + kThreads) * sizeof(float);
+  // The statistics and power kernels hold a D x D covariance in LDS (64 KiB at
+  // D = 128), above the default dynamic-LDS limit.
   if ((e = hipFuncSetAttribute((const void*)pddp_stats_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)fused_lds)) != hipSuccess)
+                               (int)lds)) != hipSuccess)
     return e;
   if ((e = hipFuncSetAttribute((const void*)pddp_power_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)power_lds)) != hipSuccess)
+                               (int)lds)) != hipSuccess)
     return e;
   for (int l = 0; l < L; ++l) {
     Level lv{l, 1 << l, parts_for(a.N, l)};
     const unsigned nb = (unsigned)(a.H * lv.nodes * lv.parts);
     if (lv.parts > 1) {
-      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), stats_lds, s, a, w, lv);
+      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), lds, s, a, w, lv);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), power_lds, s, a, w, lv);
+      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), lds, s, a, w, lv);
     } else {
-      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), fused_lds, s, a, w, lv);
+      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), lds, s, a, w, lv);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((pddp_project_kernel<T, D>), dim3(nb), dim3(kThreads), 0, s, a, w, lv);

@@ -8,10 +8,12 @@
 // all keys, 32 at a time (v_mfma_f32_32x32x16_bf16 with the group's queries as
 // the A operand, so each lane owns one key column), normalises each logit with
 // its row statistics and sums the 64 probabilities per key: mass[g][j].
-// Top-K: one workgroup per (head, group) row finds the K-th largest mass by an
-// MSB-first radix select on the fp32 bit pattern (non-negative floats order like
-// their bits), then writes the kept key ids in ascending order, ties at the
-// threshold going to the lowest ids.
+// Top-K, fused into the same wavefront: while the row is produced a 4096-bin
+// histogram of its top 12 value bits is built in LDS (non-negative floats order
+// like their bit patterns); afterwards the wave finds the bin of the K-th largest
+// mass, gathers that bin's entries, resolves the exact threshold among them and
+// writes the kept key ids in ascending order, ties at the threshold going to the
+// lowest ids.  The row is re-read while it is still in cache.
 #include <type_traits>
 
 #include "common.hpp"
@@ -31,9 +33,166 @@ struct QTile {
   __device__ static uint32_t khalf_off(int hf) { return F32 ? (uint32_t)(D / 2 * 4 * hf) : (uint32_t)(16 * hf); }
 };
 
+// Per-wave shared memory of the fused top-K: a 4096-bin histogram of the top 12
+// value bits and a candidate list (bit pattern, key id) of the histogram bin that
+// holds the K-th largest mass.
+constexpr int kHistBins = 4096;
+constexpr int kCandCap = 2048;
+struct WaveLds {
+  uint32_t hist[kHistBins];
+  uint32_t cand_bits[kCandCap];
+  int32_t cand_id[kCandCap];
+};
+
+__device__ __forceinline__ uint32_t lane_excl_scan(uint32_t x, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)v, o, 64);
+    if (lane >= o) v += y;
+  }
+  total = (uint32_t)__shfl((int)v, 63, 64);
+  return v - x;
+}
+
+// Digit (from the top) holding the kr-th largest entry of a wave-private histogram
+// of `bins` bins (a multiple of 64); returns the digit, leaves in kr the rank
+// inside it and in cnt its population.  Lane l owns bins [l*bins/64, (l+1)*bins/64).
+__device__ uint32_t pick_digit(const uint32_t* hist, int bins, uint32_t& kr, uint32_t& cnt) {
+  const int lane = threadIdx.x & 63;
+  const int per = bins / 64;
+  uint32_t t = 0;
+  for (int j = 0; j < per; ++j) t += hist[lane * per + j];
+  uint32_t above = 0;
+  int L = 0;
+  for (int l = 63; l >= 0; --l) {
+    const uint32_t tl = (uint32_t)__builtin_amdgcn_readlane((int)t, l);
+    if (above + tl >= kr || l == 0) {
+      L = l;
+      break;
+    }
+    above += tl;
+  }
+  int d = L * per;
+  cnt = 0;
+  for (int j = per - 1; j >= 0; --j) {
+    const uint32_t c = hist[L * per + j];
+    if (above + c >= kr || j == 0) {
+      d = L * per + j;
+      cnt = c;
+      break;
+    }
+    above += c;
+  }
+  kr -= above;
+  return (uint32_t)d;
+}
+
+// Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
+// id.  `w->hist` already holds the 12-bit histogram (bits 30..19) of the row.
+__device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out, WaveLds* w) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* rb = reinterpret_cast<const uint32_t*>(row);
+  uint32_t kr = (uint32_t)K, cnt = 0;
+  uint32_t prefix = pick_digit(w->hist, kHistBins, kr, cnt) << 19;
+  uint32_t pmask = 0xfffu << 19;
+  int shift = 19;
+  // Refine the prefix while too many entries share it (rare): bits 18..7, then 6..0.
+  while (cnt > (uint32_t)kCandCap && shift > 0) {
+    const int nshift = shift >= 12 ? shift - 12 : 0;
+    const int bins = 1 << (shift - nshift);
+    const int hb = bins < 64 ? 64 : bins;
+    for (int j = lane; j < hb; j += 64) w->hist[j] = 0;
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int i = lane; i < N; i += 64) {
+      const uint32_t b = rb[i];
+      if ((b & pmask) == prefix) atomicAdd(&w->hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t d = pick_digit(w->hist, hb, kr, cnt);
+    prefix |= d << nshift;
+    pmask |= (uint32_t)(bins - 1) << nshift;
+    shift = nshift;
+  }
+  // Candidates: entries matching the prefix, in ascending id order.
+  uint32_t nc = 0;
+  for (int base = 0; base < N; base += 64) {
+    const int i = base + lane;
+    const uint32_t b = i < N ? rb[i] : 0u;
+    const bool m = i < N && (b & pmask) == prefix;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(m);
+    const uint32_t pos =
+        nc + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (m && pos < (uint32_t)kCandCap) {
+      w->cand_bits[pos] = b;
+      w->cand_id[pos] = i;
+    }
+    nc += (uint32_t)__builtin_popcountll(bal);
+  }
+  if (nc > (uint32_t)kCandCap) nc = kCandCap;  // the refinement above keeps nc within the cap
+  __builtin_amdgcn_s_waitcnt(0);
+  // Resolve the remaining low bits among the candidates, 8 at a time.
+  while (shift > 0) {
+    const int nshift = shift >= 8 ? shift - 8 : 0;
+    const int bins = 1 << (shift - nshift);
+    for (int j = lane; j < 256; j += 64) w->hist[j] = 0;
+    __builtin_amdgcn_s_waitcnt(0);
+    for (uint32_t c = lane; c < nc; c += 64) {
+      const uint32_t b = w->cand_bits[c];
+      if ((b & pmask) == prefix) atomicAdd(&w->hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t d = pick_digit(w->hist, 256, kr, cnt);
+    prefix |= d << nshift;
+    pmask |= (uint32_t)(bins - 1) << nshift;
+    shift = nshift;
+  }
+  const uint32_t tau = prefix;  // the K-th largest bit pattern; keep kr of its ties
+  // Ascending compaction: 4 consecutive entries per lane, 256 per iteration.
+  uint32_t written = 0, eq_seen = 0;
+  for (int base = 0; base < N; base += 256) {
+    const int i0 = base + 4 * lane;
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = i0 + j < N ? rb[i0 + j] : 0u;
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = i0 + j < N;
+      ngt += (in && b[j] > tau) ? 1u : 0u;
+      neq += (in && b[j] == tau) ? 1u : 0u;
+    }
+    uint32_t eq_tot;
+    const uint32_t eq_before = eq_seen + lane_excl_scan(neq, eq_tot);
+    uint32_t take_eq = 0;
+    if (eq_before < kr) take_eq = min(neq, kr - eq_before);
+    uint32_t sel_tot;
+    uint32_t pos = written + lane_excl_scan(ngt + take_eq, sel_tot);
+    uint32_t left = take_eq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = i0 + j < N;
+      bool keep = in && b[j] > tau;
+      if (in && b[j] == tau && left > 0) {
+        keep = true;
+        --left;
+      }
+      if (keep) {
+        if (pos < (uint32_t)K) out[pos] = i0 + j;  // exactly K are kept; stay in the row regardless
+        ++pos;
+      }
+    }
+    written += sel_tot;
+    eq_seen += eq_tot;
+  }
+  for (int j = K + lane; j < kpad; j += 64) out[j] = -1;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   using TL = QTile<T, D>;
+  extern __shared__ WaveLds wlds[];
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int hf = lane >> 5, lm = lane & 31;
   const int items = a.hcount * a.G;
@@ -41,6 +200,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   if (blk < 0) return;
   const int item = blk * 4 + wid;
   if (item >= items) return;  // no block-level synchronisation below
+  WaveLds* w = &wlds[wid];
   const int hl = item / a.G, g = item - hl * a.G;
   const int h = a.h0 + hl;
   const int N = a.N;
@@ -48,6 +208,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   const uint32_t head_bytes = (uint32_t)((size_t)N * TL::ROWB);
   const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
   const auto rk = make_rsrc((const char*)a.k + head_off, head_bytes);
+  for (int j = lane; j < kHistBins; j += 64) w->hist[j] = 0;
 
   // Query rows of this group: lane lm holds queries lm and lm + 32 (A operand).
   int tokq[2];
@@ -97,17 +258,13 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   float* out = a.mass + ((size_t)hl * a.G + g) * (size_t)N;
   const float c = a.c;
   const int nsteps = (N + 31) >> 5;
-  u32x4 kb[TL::KCH];
-  auto load_keys = [&](int t0) {
-    const int key = t0 + lm < N ? t0 + lm : 0;
-    const uint32_t base = (uint32_t)key * TL::ROWB + TL::khalf_off(hf);
+  auto load_keys = [&](u32x4 (&kb)[TL::KCH], int t0) {
+    // keys past N read as zeros (buffer range check); their mass is never stored
+    const uint32_t base = (uint32_t)(t0 + lm) * TL::ROWB + TL::khalf_off(hf);
 #pragma unroll
     for (int cc = 0; cc < TL::KCH; ++cc) kb[cc] = bload128(rk, base + cc * TL::KSTRIDE);
   };
-  load_keys(0);
-  for (int it = 0; it < nsteps; ++it) {
-    const int t0 = it * 32;
-    f32x16 s[2];
+  auto qk = [&](f32x16 (&s)[2], const u32x4 (&kb)[TL::KCH]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       s[nt] = f32x16{};
@@ -120,181 +277,68 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
         for (int ks = 0; ks < TL::QK_STEPS; ++ks) s[nt] = mfma_bf16(as_bf16x8(q[nt][ks]), as_bf16x8(kb[ks]), s[nt]);
       }
     }
-    if (it + 1 < nsteps) load_keys(t0 + 32);
+  };
+  auto reduce_store = [&](const f32x16 (&s)[2], int t0) {
     float acc = 0.0f;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc = __builtin_fmaf(fast_exp2(__builtin_fmaf(s[nt][r], c, -rm[nt][r])), rw[nt][r], acc);
+      for (int r = 0; r < 16; ++r)
+        acc = __builtin_fmaf(fast_exp2(__builtin_fmaf(s[nt][r], c, -rm[nt][r])), rw[nt][r], acc);
     acc = pair_sum(acc);
-    if (hf == 0 && t0 + lm < N) out[t0 + lm] = acc;
+    if (hf == 0 && t0 + lm < N) {
+      out[t0 + lm] = acc;
+      atomicAdd(&w->hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
+    }
+  };
+  // Software pipeline: the MFMAs of step i+1 are issued before the exponentials
+  // of step i, so the matrix core and the VALU overlap; the single K buffer is
+  // refilled for step i+2 as soon as the step i+1 MFMAs have read it.
+  u32x4 kb[TL::KCH];
+  f32x16 sa[2], sb[2];
+  load_keys(kb, 0);
+  qk(sa, kb);
+  load_keys(kb, 32);
+  int it = 0;
+  for (; it + 2 < nsteps; it += 2) {
+    qk(sb, kb);
+    load_keys(kb, (it + 2) * 32);
+    reduce_store(sa, it * 32);
+    qk(sa, kb);
+    load_keys(kb, (it + 3) * 32);
+    reduce_store(sb, (it + 1) * 32);
   }
+  if (it + 1 < nsteps) {
+    qk(sb, kb);
+    reduce_store(sa, it * 32);
+    reduce_store(sb, (it + 1) * 32);
+  } else {
+    reduce_store(sa, it * 32);
+  }
+  // The row is complete once this wave's stores have landed; its L1 lines were
+  // never read before, so loads issued after the wait see the stored values.
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, w);
 }
 
-// ---------------------------------------------------------------------------
-// Top-K of one mass row per workgroup.
-// ---------------------------------------------------------------------------
-
-constexpr int kTopkThreads = 256;
-constexpr int kTopkWaves = kTopkThreads / 64;
-
-// Add 1 to hist[d] for every active lane, one LDS atomic per distinct digit in the
-// wave (the first radix digits of a mass row take few distinct values, so plain
-// per-lane atomics would serialise on a handful of bins).
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t d) {
-  uint64_t todo = __builtin_amdgcn_ballot_w64(active);
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
-    const uint64_t same = __builtin_amdgcn_ballot_w64(active && d == ld);
-    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[ld], (uint32_t)__builtin_popcountll(same));
-    todo &= ~same;
-  }
-}
-
-// Inclusive prefix sum over the 256 threads of the block; returns the block total.
-__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& incl) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)v, o, 64);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) wsum[wid] = v;
-  __syncthreads();
-  uint32_t before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t t = wsum[w];
-    if (w < wid) before += t;
-    total += t;
-  }
-  __syncthreads();
-  incl = v + before;
-  return total;
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[kTopkWaves];
-  __shared__ uint32_t sel_state[3];
-  const int row = blockIdx.x;
-  const int N = a.N, K = a.K;
-  const uint32_t* m = reinterpret_cast<const uint32_t*>(a.mass + (size_t)row * N);
-  int32_t* out = a.idx + (size_t)row * a.kpad;
-  const int tid = threadIdx.x;
-
-  // Radix select of the K-th largest bit pattern, 8 bits per pass, MSB first.
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t kr = (uint32_t)K;  // rank (1-based, from the top) still to locate
-  uint32_t eq_total = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int base = 0; base < N; base += kTopkThreads) {
-      const int i = base + tid;
-      uint32_t bits = i < N ? m[i] : 0u;
-      const bool act = i < N && (bits & pmask) == prefix;
-      hist_add(hist, act, (bits >> shift) & 255u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= kr) break;
-        above += hist[d];
-      }
-      sel_state[0] = (uint32_t)d;
-      sel_state[1] = kr - above;
-      sel_state[2] = hist[d];
-    }
-    __syncthreads();
-    prefix |= sel_state[0] << shift;
-    pmask |= 255u << shift;
-    kr = sel_state[1];
-    eq_total = sel_state[2];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;
-  // kr of the eq_total entries equal to tau are kept (the lowest ids).
-  const bool all_ties = kr == eq_total;
-
-  // Ascending compaction, 16 consecutive entries per thread per tile.
-  constexpr int E = 16;
-  uint32_t written = 0, eq_seen = 0;
-  for (int base = 0; base < N; base += kTopkThreads * E) {
-    const int i0 = base + tid * E;
-    uint32_t bits[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) bits[e] = i0 + e < N ? m[i0 + e] : 0u;
-    uint32_t ne = 0, ngt = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool in = i0 + e < N;
-      ngt += (in && bits[e] > tau) ? 1u : 0u;
-      ne += (in && bits[e] == tau) ? 1u : 0u;
-    }
-    uint32_t eq_before = 0;
-    if (!all_ties) {
-      uint32_t incl;
-      const uint32_t tot = block_scan(ne, wsum, incl);
-      eq_before = eq_seen + incl - ne;
-      eq_seen += tot;
-    }
-    // entries kept by this thread
-    uint32_t take_eq = ne;
-    if (!all_ties) {
-      const uint32_t room = kr > eq_before ? kr - eq_before : 0u;
-      take_eq = ne < room ? ne : room;
-    }
-    const uint32_t nsel = ngt + take_eq;
-    uint32_t incl;
-    const uint32_t tot = block_scan(nsel, wsum, incl);
-    uint32_t pos = written + incl - nsel;
-    uint32_t eq_left = take_eq;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool in = i0 + e < N;
-      bool keep = in && bits[e] > tau;
-      if (in && bits[e] == tau && eq_left > 0) {
-        keep = true;
-        --eq_left;
-      }
-      if (keep) {
-        if (pos < (uint32_t)K) out[pos] = i0 + e;  // exactly K are kept; stay inside the row regardless
-        ++pos;
-      }
-    }
-    written += tot;
-  }
-  for (int j = K + tid; j < a.kpad; j += kTopkThreads) out[j] = -1;
+template <typename T, int D>
+hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
+  const int items = a.hcount * a.G;
+  const int blocks = xcd_grid((items + 3) / 4);
+  const size_t lds = 4 * sizeof(WaveLds);
+  hipError_t e = hipFuncSetAttribute((const void*)group_mass_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((group_mass_kernel<T, D>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s) {
-  const int items = a.hcount * a.G;
-  const int blocks = xcd_grid((items + 3) / 4);
-  if (dtype == DT_BF16) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((group_mass_kernel<__bf16, 128>), dim3(blocks), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((group_mass_kernel<__bf16, 64>), dim3(blocks), dim3(256), 0, s, a);
-  } else {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((group_mass_kernel<float, 128>), dim3(blocks), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((group_mass_kernel<float, 64>), dim3(blocks), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.rows), dim3(kTopkThreads), 0, s, a);
-  return hipGetLastError();
+  if (dtype == DT_BF16) return head_dim == 128 ? launch_mass_t<__bf16, 128>(a, s) : launch_mass_t<__bf16, 64>(a, s);
+  return head_dim == 128 ? launch_mass_t<float, 128>(a, s) : launch_mass_t<float, 64>(a, s);
 }
 
 }  // namespace mcs
