@@ -41,7 +41,8 @@ struct MassArgs {
   const int32_t* perm;     // [H][N]
   const float2* stats;     // [H][N] row statistics from pass 1 (or null: use lse)
   const float* lse;        // [H][N] natural-log logsumexp (used when stats is null)
-  float* mass;             // [hcount][G][N] scratch rows
+  float* mass;             // [hcount][G][ldm] scratch rows
+  int ldm;                 // row stride of mass: N rounded up to a multiple of 4
   int32_t* idx;            // [H][G][kpad] output
   int h0, hcount, N, G, K, kpad;
   float c;                 // scale * log2(e)

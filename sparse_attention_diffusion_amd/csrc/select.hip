@@ -89,6 +89,26 @@ __device__ uint32_t pick_digit(const uint32_t* hist, int bins, uint32_t& kr, uin
   return (uint32_t)d;
 }
 
+constexpr int kUnroll = 8;
+constexpr int kBatch = 256 * kUnroll;
+
+// Entries [base, base + kBatch) of a row: lane l gets entries base + 256*u + 4*l + j.
+// Entries past N read as 0 (they are masked by the callers).
+__device__ __forceinline__ void load_batch(const uint32_t* rb, int N, int base, uint32_t (&b)[kUnroll][4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int i0 = base + 256 * u + 4 * lane;
+    if (i0 + 3 < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(rb + i0);
+      b[u][0] = v[0]; b[u][1] = v[1]; b[u][2] = v[2]; b[u][3] = v[3];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[u][j] = i0 + j < N ? rb[i0 + j] : 0u;
+    }
+  }
+}
+
 // Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
 // id.  `w->hist` already holds the 12-bit histogram (bits 30..19) of the row.
 __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out, WaveLds* w) {
@@ -115,20 +135,32 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
     pmask |= (uint32_t)(bins - 1) << nshift;
     shift = nshift;
   }
-  // Candidates: entries matching the prefix, in ascending id order.
+  // Candidates: entries matching the prefix, in ascending id order.  The row is
+  // read in batches of 8 x 256 entries (8 independent 16-byte loads per lane).
   uint32_t nc = 0;
-  for (int base = 0; base < N; base += 64) {
-    const int i = base + lane;
-    const uint32_t b = i < N ? rb[i] : 0u;
-    const bool m = i < N && (b & pmask) == prefix;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(m);
-    const uint32_t pos =
-        nc + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (m && pos < (uint32_t)kCandCap) {
-      w->cand_bits[pos] = b;
-      w->cand_id[pos] = i;
+  for (int base = 0; base < N; base += kBatch) {
+    uint32_t b[kUnroll][4];
+    load_batch(rb, N, base, b);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i0 = base + 256 * u + 4 * lane;
+      uint32_t nm = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nm += (i0 + j < N && (b[u][j] & pmask) == prefix) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t pos = nc + lane_excl_scan(nm, tot);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < N && (b[u][j] & pmask) == prefix) {
+          if (pos < (uint32_t)kCandCap) {
+            w->cand_bits[pos] = b[u][j];
+            w->cand_id[pos] = i0 + j;
+          }
+          ++pos;
+        }
+      }
+      nc += tot;
     }
-    nc += (uint32_t)__builtin_popcountll(bal);
   }
   if (nc > (uint32_t)kCandCap) nc = kCandCap;  // the refinement above keeps nc within the cap
   __builtin_amdgcn_s_waitcnt(0);
@@ -149,42 +181,45 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
     shift = nshift;
   }
   const uint32_t tau = prefix;  // the K-th largest bit pattern; keep kr of its ties
-  // Ascending compaction: 4 consecutive entries per lane, 256 per iteration.
+  // Ascending compaction, same batching: 4 consecutive entries per lane.
   uint32_t written = 0, eq_seen = 0;
-  for (int base = 0; base < N; base += 256) {
-    const int i0 = base + 4 * lane;
-    uint32_t b[4];
+  for (int base = 0; base < N; base += kBatch) {
+    uint32_t bb[kUnroll][4];
+    load_batch(rb, N, base, bb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = i0 + j < N ? rb[i0 + j] : 0u;
-    uint32_t ngt = 0, neq = 0;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i0 = base + 256 * u + 4 * lane;
+      const uint32_t* b = bb[u];
+      uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool in = i0 + j < N;
-      ngt += (in && b[j] > tau) ? 1u : 0u;
-      neq += (in && b[j] == tau) ? 1u : 0u;
-    }
-    uint32_t eq_tot;
-    const uint32_t eq_before = eq_seen + lane_excl_scan(neq, eq_tot);
-    uint32_t take_eq = 0;
-    if (eq_before < kr) take_eq = min(neq, kr - eq_before);
-    uint32_t sel_tot;
-    uint32_t pos = written + lane_excl_scan(ngt + take_eq, sel_tot);
-    uint32_t left = take_eq;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool in = i0 + j < N;
-      bool keep = in && b[j] > tau;
-      if (in && b[j] == tau && left > 0) {
-        keep = true;
-        --left;
+      for (int j = 0; j < 4; ++j) {
+        const bool in = i0 + j < N;
+        ngt += (in && b[j] > tau) ? 1u : 0u;
+        neq += (in && b[j] == tau) ? 1u : 0u;
       }
-      if (keep) {
-        if (pos < (uint32_t)K) out[pos] = i0 + j;  // exactly K are kept; stay in the row regardless
-        ++pos;
+      uint32_t eq_tot;
+      const uint32_t eq_before = eq_seen + lane_excl_scan(neq, eq_tot);
+      uint32_t take_eq = 0;
+      if (eq_before < kr) take_eq = min(neq, kr - eq_before);
+      uint32_t sel_tot;
+      uint32_t pos = written + lane_excl_scan(ngt + take_eq, sel_tot);
+      uint32_t left = take_eq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = i0 + j < N;
+        bool keep = in && b[j] > tau;
+        if (in && b[j] == tau && left > 0) {
+          keep = true;
+          --left;
+        }
+        if (keep) {
+          if (pos < (uint32_t)K) out[pos] = i0 + j;  // exactly K are kept; stay in the row regardless
+          ++pos;
+        }
       }
+      written += sel_tot;
+      eq_seen += eq_tot;
     }
-    written += sel_tot;
-    eq_seen += eq_tot;
   }
   for (int j = K + lane; j < kpad; j += 64) out[j] = -1;
 }
@@ -255,7 +290,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
       rw[nt][r] = lane_read(my_w[nt], src);
     }
 
-  float* out = a.mass + ((size_t)hl * a.G + g) * (size_t)N;
+  float* out = a.mass + ((size_t)hl * a.G + g) * (size_t)a.ldm;  // rows 16-byte aligned
   const float c = a.c;
   const int nsteps = (N + 31) >> 5;
   auto load_keys = [&](u32x4 (&kb)[TL::KCH], int t0) {
