@@ -1,0 +1,172 @@
+"""Host-side checks of the meta-cache's stream/event protocol (no GPU).
+
+A fake backend simulates two in-order streams with random operation durations:
+every op starts when its stream is free and all events it waits on have fired.
+Buffers carry (layer, version) tags; the test replays the trajectory call
+pattern and checks that every reuse reads the entry of the right layer from its
+latest anchor, and that no copy or kernel overlaps a conflicting access."""
+import random
+
+import pytest
+
+from sparse_attention_diffusion_amd import MCS_COPY_D2H, MCS_COPY_H2D
+from sparse_attention_diffusion_amd.cache import MetaCache
+from sparse_attention_diffusion_amd.trajectory import step_kind
+
+
+class Buf:
+    def __init__(self, name):
+        self.name = name
+        self.writes = [(0.0, None)]   # (time, tag)
+        self.accesses = []            # (t0, t1, kind)
+
+    def value_at(self, t):
+        return max((w for w in self.writes if w[0] <= t), key=lambda w: w[0])[1]
+
+    def access(self, t0, t1, kind):
+        for a0, a1, k in self.accesses:
+            if (kind == "w" or k == "w") and a0 < t1 and t0 < a1:
+                raise AssertionError(f"{self.name}: {kind} [{t0:.2f},{t1:.2f}) overlaps {k} [{a0:.2f},{a1:.2f})")
+        self.accesses.append((t0, t1, kind))
+
+    def numel(self):
+        return 1
+
+    def element_size(self):
+        return 1
+
+
+class Stream:
+    def __init__(self, name):
+        self.name = name
+        self.t = 0.0
+
+
+class Event:
+    def __init__(self):
+        self.time = None
+
+
+class FakeBackend:
+    def __init__(self, seed):
+        self.rng = random.Random(seed)
+        self.compute = Stream("compute")
+        self.side = Stream("side")
+        self.n = 0
+
+    def compute_stream(self):
+        return self.compute
+
+    def event(self):
+        return Event()
+
+    def record(self, ev, stream):
+        ev.time = stream.t
+
+    def wait(self, stream, ev):
+        assert ev.time is not None, "waiting on an event that was never recorded"
+        stream.t = max(stream.t, ev.time)
+
+    def copy(self, dst, src, kind, stream):
+        dur = self.rng.uniform(0.5, 4.0)
+        t0, t1 = stream.t, stream.t + dur
+        src.access(t0, t1, "r")
+        dst.access(t0, t1, "w")
+        dst.writes.append((t1, src.value_at(t0)))
+        stream.t = t1
+
+    def kernel(self, reads=(), writes=(), tag=None):
+        dur = self.rng.uniform(0.5, 3.0)
+        t0, t1 = self.compute.t, self.compute.t + dur
+        vals = [b.value_at(t0) for b in reads]
+        for b in reads:
+            b.access(t0, t1, "r")
+        for b in writes:
+            b.access(t0, t1, "w")
+            b.writes.append((t1, tag))
+        self.compute.t = t1
+        return vals
+
+    def empty_device(self, shape, dtype):
+        self.n += 1
+        return Buf(f"dev{self.n}")
+
+    def empty_host(self, shape, dtype):
+        self.n += 1
+        return Buf(f"host{self.n}")
+
+
+SHAPES = {"perm": ((1,), None), "idx": ((1,), None), "resid": ((1,), None)}
+
+
+def replay(cache, be, layers, steps, warmup=2, interval=3):
+    version = {}
+    for step in range(steps):
+        kind = step_kind(step, warmup, interval)
+        for layer in range(layers):
+            if kind == "anchor":
+                buf = cache.anchor_buffers(layer, busy_layer=layer - 1)
+                version[layer] = (layer, step)
+                be.kernel(writes=list(buf.values()), tag=version[layer])
+                cache.commit_anchor(layer)
+                cache.release(layer)
+            elif kind == "reuse":
+                buf = cache.get(layer)
+                vals = be.kernel(reads=list(buf.values()))
+                assert vals == [version[layer]] * 3, (step, layer, vals, version[layer])
+                cache.release(layer)
+            nxt_step, nxt_layer = (step, layer + 1) if layer + 1 < layers else (step + 1, 0)
+            if nxt_step < steps and step_kind(nxt_step, warmup, interval) == "reuse":
+                cache.prefetch(nxt_layer, busy_layer=layer)
+
+
+@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("layers,slots", [(1, 1), (2, 2), (5, 2), (6, 3)])
+def test_offload_protocol_orders_every_access(seed, layers, slots):
+    be = FakeBackend(seed)
+    cache = MetaCache(layers, SHAPES, be, offload=True, device_slots=slots)
+    replay(cache, be, layers, steps=12)
+    assert cache.bytes_d2h > 0 and (layers <= slots or cache.bytes_h2d > 0)
+
+
+def test_resident_mode_needs_no_copies():
+    be = FakeBackend(0)
+    cache = MetaCache(4, SHAPES, be, offload=False)
+    replay(cache, be, 4, steps=10)
+    assert cache.bytes_d2h == 0 and cache.bytes_h2d == 0
+
+
+def test_reuse_before_any_anchor_is_an_error():
+    be = FakeBackend(0)
+    cache = MetaCache(2, SHAPES, be, offload=True)
+    with pytest.raises(RuntimeError):
+        cache.get(0)
+    with pytest.raises(RuntimeError):
+        cache.prefetch(1)
+
+
+def test_a_dropped_wait_is_detected():
+    # Plant a mistake in the protocol (the reuse no longer waits for the prefetch)
+    # and check that the simulation catches the race.
+    be = FakeBackend(3)
+    cache = MetaCache(4, SHAPES, be, offload=True, device_slots=2)
+    real_wait = be.wait
+
+    def lazy_wait(stream, ev):
+        if stream is be.compute:
+            return  # compute stream ignores every event
+        real_wait(stream, ev)
+
+    be.wait = lazy_wait
+    with pytest.raises(AssertionError):
+        replay(cache, be, 4, steps=12)
+
+
+def test_copy_kinds():
+    be = FakeBackend(1)
+    kinds = []
+    orig = be.copy
+    be.copy = lambda d, s, k, st: (kinds.append(k), orig(d, s, k, st))
+    cache = MetaCache(3, SHAPES, be, offload=True, device_slots=2)
+    replay(cache, be, 3, steps=8)
+    assert set(kinds) == {MCS_COPY_D2H, MCS_COPY_H2D}
