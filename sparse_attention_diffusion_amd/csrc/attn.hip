@@ -141,40 +141,60 @@ struct State {
 };
 
 // S^T of one 32-key step (rows: the step's keys, columns: the group's 64 queries).
-// The group's Q operands live in LDS in lane order: chunk (nt, c) of lane l at
-// ((nt * KCH + c) * 64 + l) * 16 bytes, so every read is one conflict-free
-// ds_read_b128 and Q costs no registers between steps.
-typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
-
 template <typename T, int D>
-__device__ __forceinline__ u32x4 q_chunk(lds_u32x4* qs, int nt, int c) {
-  return qs[(nt * Tile<T, D>::KCH + c) * 64];
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void qk(f32x16 (&s)[2], const KV<T, D>& b, const u32x4* qs_base, int lane) {
+__device__ __forceinline__ void qk(f32x16 (&s)[2], const KV<T, D>& b, const u32x4 (&q)[2][Tile<T, D>::KCH]) {
   using TL = Tile<T, D>;
-  // The LDS address is made opaque on every step so the compiler neither forwards
-  // the staging stores nor hoists Q back into registers (which would push the
-  // loop into register spills); the reads themselves can still be batched.
-  uint32_t qa = (uint32_t)(uintptr_t)(qs_base + lane);
-  asm volatile("" : "+v"(qa));
-  lds_u32x4* qs = (lds_u32x4*)(uintptr_t)qa;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     s[nt] = f32x16{};
     if constexpr (TL::F32) {
 #pragma unroll
-      for (int c = 0; c < TL::KCH; ++c) {
-        const u32x4 qc = q_chunk<T, D>(qs, nt, c);
+      for (int c = 0; c < TL::KCH; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          s[nt] = mfma_f32(__uint_as_float(b.k[c][j]), __uint_as_float(qc[j]), s[nt]);
-      }
+          s[nt] = mfma_f32(__uint_as_float(b.k[c][j]), __uint_as_float(q[nt][c][j]), s[nt]);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < TL::QK_STEPS; ++ks)
-        s[nt] = mfma_bf16(as_bf16x8(b.k[ks]), as_bf16x8(q_chunk<T, D>(qs, nt, ks)), s[nt]);
+      for (int ks = 0; ks < TL::QK_STEPS; ++ks) s[nt] = mfma_bf16(as_bf16x8(b.k[ks]), as_bf16x8(q[nt][ks]), s[nt]);
+    }
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int t0, int nkeys, int hf) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (t0 + 16 * hf + r >= nkeys) s[nt][r] = -INFINITY;
+}
+
+// Probabilities exp2(s*c - m) with the offsets m fixed, their bf16 packing for the
+// PV product, and the row sums.
+template <typename T, int D, bool PV, bool EXACT_SUM>
+__device__ __forceinline__ void probs(State<T, D, PV>& st, f32x16 (&s)[2], uint32_t (&pk)[2][8], float c) {
+  using TL = Tile<T, D>;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float moff = st.m[nt];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[nt][r] = fast_exp2(__builtin_fmaf(s[nt][r], c, -moff));
+    if constexpr (!TL::F32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[nt][i] = pack_bf16x2(s[nt][2 * i], s[nt][2 * i + 1]);
+    }
+    if constexpr (EXACT_SUM || TL::F32) {
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls += s[nt][r];
+      st.l[nt] += ls;
+    } else {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      float ls = st.l[nt];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[nt][i]), one, ls, false);
+      st.l[nt] = ls;
     }
   }
 }
@@ -280,96 +300,142 @@ __device__ __forceinline__ void pv(State<T, D, PV>& st, const f32x16 (&p)[2], co
   }
 }
 
-template <typename T, int D, bool GATHER, int EPI, bool PV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_kernel(AttnArgs a) {
-  using TL = Tile<T, D>;
-  const int lane = threadIdx.x & 63, wid = wave_id();
-  const int hf = lane >> 5, lm = lane & 31;
-  const int items = a.H * a.G;
-  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
-  if (blk < 0) return;
-  const int item = blk * 4 + wid;
-  if (item >= items) return;  // no block-level synchronisation below
-  const int h = item / a.G, g = item - h * a.G;
-  const int N = a.N;
-  const size_t head_off = (size_t)h * N * TL::ROWB;
-  const uint32_t head_bytes = (uint32_t)((size_t)N * TL::ROWB);
-  const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
-  const auto rk = make_rsrc((const char*)a.k + head_off, head_bytes);
-  const auto rv = make_rsrc((const char*)a.v + head_off, head_bytes);
-  const int nkeys = a.nkeys;
-  const auto ridx = GATHER ? make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad, (uint32_t)a.kpad * 4u)
-                           : make_rsrc(nullptr, 0);
+// Per-wave context of one query group.
+template <typename T, int D, bool GATHER>
+struct Ctx {
+  __amdgpu_buffer_rsrc_t rk, rv, ridx;
+  int nkeys, lm, hf;
+  float c;
+};
 
-  // This lane's two query columns (queries lm and lm + 32 of the group).
-  int tokq[2];
-  bool qvalid[2];
+// Fixed-offset pass over the group's key list.  Each query's offset is the
+// maximum of its first 32 logits plus kMargin (log2 units); every later
+// probability is exp2(s*c - offset) with no running maximum and no rescaling of
+// O, so a step is one straight basic block of MFMAs and VALU work.  A logit more
+// than 2^(127 - kMargin) above the first tile's maximum overflows the row sum,
+// which the caller detects and answers with the online pass below.
+constexpr float kMargin = 16.0f;
+
+template <typename T, int D, bool GATHER, bool PV>
+__device__ __forceinline__ void fixed_step(State<T, D, PV>& st, const Ctx<T, D, GATHER>& x,
+                                           const u32x4 (&q)[2][Tile<T, D>::KCH], KV<T, D>& b, const Idx& inext,
+                                           Idx& ilater, int it) {
+  // Step `it` with K/V already in flight in b; inext holds the keys of step it+1,
+  // ilater receives those of step it+2.  The index loads are issued first so
+  // that waiting for them never waits for this step's K/V gathers (the vector
+  // memory counter retires in order).
+  constexpr bool EXACT = !GATHER;
+  load_idx<GATHER>(ilater, x.ridx, (it + 2) * 32, x.lm, x.hf);
+  f32x16 s[2];
+  uint32_t pk[2][8];
+  __builtin_amdgcn_sched_barrier(0);
+  qk<T, D>(s, b, q);
+  load_k<T, D>(b, inext, x.rk, x.hf);
+  // keep the gathers where they are: sinking them toward the end of the step
+  // (which the scheduler does to shorten live ranges) exposes their latency
+  __builtin_amdgcn_sched_barrier(0);
+  probs<T, D, PV, EXACT>(st, s, pk, x.c);
+  if constexpr (PV) {
+    pv<T, D, PV>(st, s, pk, b);
+    load_v<T, D>(b, inext, x.rv, x.lm);
+  }
+}
+
+template <typename T, int D, bool GATHER, bool PV>
+__device__ __forceinline__ void pass_fixed(State<T, D, PV>& st, const Ctx<T, D, GATHER>& x,
+                                           const u32x4 (&q)[2][Tile<T, D>::KCH]) {
+  constexpr bool EXACT = !GATHER;
+  Idx ia, ib;
+  KV<T, D> b;
+  const int nsteps = (x.nkeys + 31) >> 5;
+  load_idx<GATHER>(ia, x.ridx, 0, x.lm, x.hf);
+  load_k<T, D>(b, ia, x.rk, x.hf);
+  if constexpr (PV) load_v<T, D>(b, ia, x.rv, x.lm);
+  load_idx<GATHER>(ia, x.ridx, 32, x.lm, x.hf);
+  load_idx<GATHER>(ib, x.ridx, 64, x.lm, x.hf);
+  {  // first step: fixes the offsets
+    f32x16 s[2];
+    uint32_t pk[2][8];
+    qk<T, D>(s, b, q);
+    if (nsteps > 1) load_k<T, D>(b, ia, x.rk, x.hf);
+    if (nsteps == 1) mask_tail<0>(s, 0, x.nkeys, x.hf);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int slot = g * 64 + lm + 32 * nt;
-    qvalid[nt] = slot < N;
-    tokq[nt] = qvalid[nt] ? (a.perm ? a.perm[(size_t)h * N + slot] : slot) : 0;
-    if (tokq[nt] < 0 || tokq[nt] >= N) {  // not a token (corrupt perm): compute nothing for it
-      qvalid[nt] = false;
-      tokq[nt] = 0;
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = s[nt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+      st.m[nt] = pair_max(mx) * x.c + kMargin;
+    }
+    probs<T, D, PV, EXACT>(st, s, pk, x.c);
+    if constexpr (PV) {
+      pv<T, D, PV>(st, s, pk, b);
+      if (nsteps > 1) load_v<T, D>(b, ia, x.rv, x.lm);
     }
   }
-  // Stage this wave's Q operands in its LDS slice (written and read by this wave only).
-  __shared__ u32x4 q_lds[4][2 * TL::KCH * 64];
-  u32x4* qs = q_lds[wid];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
-#pragma unroll
-    for (int c = 0; c < TL::KCH; ++c) qs[(nt * TL::KCH + c) * 64 + lane] = bload128(rq, qb + c * TL::KSTRIDE);
+  ia = ib;
+  // Middle steps: no masking, no branches around the prefetches (reads past the
+  // key list return zeros or valid rows that are never used).  ia holds the keys
+  // of step it+1; the step loads those of it+2 into ib first thing, so the copy
+  // at the end waits only for that load, not for the K/V gathers issued after it.
+#pragma unroll 1
+  for (int it = 1; it + 1 < nsteps; ++it) {
+    fixed_step<T, D, GATHER, PV>(st, x, q, b, ia, ib, it);
+    ia = ib;
   }
+  if (nsteps > 1) {
+    f32x16 s[2];
+    uint32_t pk[2][8];
+    qk<T, D>(s, b, q);
+    mask_tail<0>(s, (nsteps - 1) * 32, x.nkeys, x.hf);
+    probs<T, D, PV, EXACT>(st, s, pk, x.c);
+    if constexpr (PV) pv<T, D, PV>(st, s, pk, b);
+  }
+}
 
-  State<T, D, PV> st;
+// Online pass with a running maximum and lazy rescaling (the offset moves only
+// when the maximum grows by more than 2^8).  Used only for groups whose
+// fixed-offset pass overflowed.
+template <typename T, int D, bool GATHER, bool PV>
+__device__ __attribute__((noinline)) void pass_online(State<T, D, PV>& st, const Ctx<T, D, GATHER>& x,
+                                                      const u32x4 (&q)[2][Tile<T, D>::KCH]) {
+  constexpr bool EXACT = !GATHER;
+  Idx ix;
+  KV<T, D> b;
+  const int nsteps = (x.nkeys + 31) >> 5;
+  for (int it = 0; it < nsteps; ++it) {
+    load_idx<GATHER>(ix, x.ridx, it * 32, x.lm, x.hf);
+    load_k<T, D>(b, ix, x.rk, x.hf);
+    if constexpr (PV) load_v<T, D>(b, ix, x.rv, x.lm);
+    f32x16 s[2];
+    uint32_t pk[2][8];
+    qk<T, D>(s, b, q);
+    if (it + 1 == nsteps)
+      softmax<T, D, PV, EXACT, true>(st, s, pk, it * 32, x.nkeys, x.c, x.hf);
+    else
+      softmax<T, D, PV, EXACT, false>(st, s, pk, it * 32, x.nkeys, x.c, x.hf);
+    if constexpr (PV) pv<T, D, PV>(st, s, pk, b);
+  }
+}
+
+template <typename T, int D, bool PV>
+__device__ __forceinline__ void state_init(State<T, D, PV>& st) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     st.m[nt] = -INFINITY;
     st.l[nt] = 0.0f;
     if constexpr (PV) {
 #pragma unroll
-      for (int cc = 0; cc < TL::VEC; ++cc) st.o[nt][cc] = f32x16{};
+      for (int cc = 0; cc < Tile<T, D>::VEC; ++cc) st.o[nt][cc] = f32x16{};
     }
   }
+}
 
-  // Software pipeline with one K/V buffer: the next step's K rows are requested as
-  // soon as this step's S^T has consumed the K registers, its V rows as soon as
-  // the PV product has consumed the V registers, and the indices of the step
-  // after that right behind them.
-  Idx ix;
-  KV<T, D> b;
-  const int nsteps = (nkeys + 31) >> 5;
-  load_idx<GATHER>(ix, ridx, 0, lm, hf);
-  load_k<T, D>(b, ix, rk, hf);
-  if constexpr (PV) load_v<T, D>(b, ix, rv, lm);
-  load_idx<GATHER>(ix, ridx, 32, lm, hf);
-  // Steps before the last: no masking, no branches around the prefetches (reads
-  // past the key list return zeros or valid rows that are never used).
-  for (int it = 0; it + 1 < nsteps; ++it) {
-    f32x16 s[2];
-    uint32_t pk[2][8];
-    qk<T, D>(s, b, qs, lane);
-    load_k<T, D>(b, ix, rk, hf);
-    softmax<T, D, PV, !GATHER, false>(st, s, pk, it * 32, nkeys, a.c, hf);
-    if constexpr (PV) {
-      pv<T, D, PV>(st, s, pk, b);
-      load_v<T, D>(b, ix, rv, lm);
-    }
-    load_idx<GATHER>(ix, ridx, (it + 2) * 32, lm, hf);
-  }
-  {
-    f32x16 s[2];
-    uint32_t pk[2][8];
-    qk<T, D>(s, b, qs, lane);
-    softmax<T, D, PV, !GATHER, true>(st, s, pk, (nsteps - 1) * 32, nkeys, a.c, hf);
-    if constexpr (PV) pv<T, D, PV>(st, s, pk, b);
-  }
-
-  // Row statistics: combine the two lane halves' partial sums.
+// Row statistics, normalisation and the epilogue stores of one group.
+template <typename T, int D, int EPI, bool PV>
+__device__ __forceinline__ void finish(const State<T, D, PV>& st, const AttnArgs& a, int h, int g, const int (&tokq)[2],
+                                       const bool (&qvalid)[2], int lm, int hf) {
+  using TL = Tile<T, D>;
+  const int N = a.N;
   float inv[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -400,10 +466,10 @@ void attn_kernel(AttnArgs a) {
           float* out = (float*)a.o + base;
 #pragma unroll
           for (int cc = 0; cc < TL::VEC; ++cc) {
-            float x = vals[cc];
-            if constexpr (EPI == EPI_ADD) x += rin[base + cc];
-            if constexpr (EPI == EPI_RESID) x = rin[base + cc] - x;
-            out[cc] = x;
+            float v = vals[cc];
+            if constexpr (EPI == EPI_ADD) v += rin[base + cc];
+            if constexpr (EPI == EPI_RESID) v = rin[base + cc] - v;
+            out[cc] = v;
           }
         } else {
           const __bf16* rin = (const __bf16*)a.rin;
@@ -423,6 +489,66 @@ void attn_kernel(AttnArgs a) {
         }
       }
     }
+  }
+}
+
+template <typename T, int D, bool GATHER, int EPI, bool PV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_kernel(AttnArgs a) {
+  using TL = Tile<T, D>;
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int hf = lane >> 5, lm = lane & 31;
+  const int items = a.H * a.G;
+  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
+  if (blk < 0) return;
+  const int item = blk * 4 + wid;
+  if (item >= items) return;  // no block-level synchronisation below
+  const int h = item / a.G, g = item - h * a.G;
+  const int N = a.N;
+  const size_t head_off = (size_t)h * N * TL::ROWB;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * TL::ROWB);
+  const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
+  Ctx<T, D, GATHER> x;
+  x.rk = make_rsrc((const char*)a.k + head_off, head_bytes);
+  x.rv = make_rsrc((const char*)a.v + head_off, head_bytes);
+  x.ridx = GATHER ? make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad, (uint32_t)a.kpad * 4u) : make_rsrc(nullptr, 0);
+  x.nkeys = a.nkeys;
+  x.lm = lm;
+  x.hf = hf;
+  x.c = a.c;
+
+  // This lane's two query columns (queries lm and lm + 32 of the group).
+  int tokq[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int slot = g * 64 + lm + 32 * nt;
+    qvalid[nt] = slot < N;
+    tokq[nt] = qvalid[nt] ? (a.perm ? a.perm[(size_t)h * N + slot] : slot) : 0;
+    if (tokq[nt] < 0 || tokq[nt] >= N) {  // not a token (corrupt perm): compute nothing for it
+      qvalid[nt] = false;
+      tokq[nt] = 0;
+    }
+  }
+  u32x4 q[2][TL::KCH];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
+#pragma unroll
+    for (int c = 0; c < TL::KCH; ++c) q[nt][c] = bload128(rq, qb + c * TL::KSTRIDE);
+  }
+
+  State<T, D, PV> st;
+  state_init<T, D, PV>(st);
+  pass_fixed<T, D, GATHER, PV>(st, x, q);
+  const bool ok = __builtin_isfinite(st.l[0]) && __builtin_isfinite(st.l[1]);
+  if (__builtin_amdgcn_ballot_w64(!ok)) {
+    State<T, D, PV> so;
+    state_init<T, D, PV>(so);
+    pass_online<T, D, GATHER, PV>(so, x, q);
+    finish<T, D, EPI, PV>(so, a, h, g, tokq, qvalid, lm, hf);
+  } else {
+    finish<T, D, EPI, PV>(st, a, h, g, tokq, qvalid, lm, hf);
   }
 }
 
