@@ -552,6 +552,447 @@ void attn_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path with K/V staged through LDS.
+//
+// Fetching a K row straight into the MFMA operand layout puts a different row
+// in every lane of a quad, which costs the texture-address unit four cycles per
+// quad: the gathers of a step, not the MFMAs, set the pace.  Here every step's
+// 32 K rows and 32 V rows are copied global -> LDS with buffer_load ... lds,
+// each lane quad reading 64 contiguous bytes of one row (one cycle per quad),
+// and the operands are read from LDS: K with ds_read_b128, V with the gfx950
+// transposing read ds_read_b64_tr_b16, which hands every lane one dimension of
+// four keys, i.e. the PV B-operand layout, with no register shuffles.
+//
+// Tile geometry (one K or V tile = the 32 rows of one step):
+//   a DMA instruction moves 1 KiB = RPI rows; lane j of instruction i fetches
+//   16-byte chunk (j % LPR) ^ swz(g) of step entry NI*g + i, g = j / LPR, and it
+//   lands at LDS offset i*BLK + 16*j.  So entry e sits in block e % NI, row
+//   e / NI, and its chunk x at position x ^ swz(e / NI).  The 32-byte skew
+//   between blocks and the XOR swizzle inside 64-byte groups spread the rows a
+//   ds_read touches together over the LDS banks; the swizzle never leaves a
+//   64-byte group, so a quad still reads one contiguous 64-byte piece.
+//   Entry e of the step is row e of S^T, so the accumulator register r of lane
+//   half hf holds entry 8*(r/4) + 4*hf + r%4.
+// Two stages (separate LDS arrays, so the compiler's wait counting can tell the
+// in-flight copy of step i+1 from the one step i reads) alternate.
+template <int D>
+struct LT {
+  static constexpr int ROWB = D * 2;
+  static constexpr int LPR = ROWB / 16;   // lanes per row in a DMA
+  static constexpr int RPI = 64 / LPR;    // rows per DMA instruction
+  static constexpr int NI = 32 / RPI;     // DMA instructions per tile
+  static constexpr int BLK = 1024 + 32;
+  static constexpr int TILE = NI * BLK;
+  static constexpr int KCH = D / 16;      // QK k-chunks of 16 dims
+  static constexpr int VT = D / 32;       // PV output tiles of 32 dims
+  // epilogue: half of the group's O (32 queries, fp32) with a 16-byte row skew
+  static constexpr int OPITCH = D * 4 + 16;
+  static constexpr int STAGE = (2 * TILE > 32 * OPITCH) ? 2 * TILE : 32 * OPITCH;
+  __device__ static int swz(int g) { return (g * ROWB / 256) & 3; }
+  __device__ static int off(int e, int x) { return (e % NI) * BLK + (e / NI) * ROWB + 16 * (x ^ swz(e / NI)); }
+};
+
+#define LDSP __attribute__((address_space(3)))
+
+template <int D>
+struct LKeys {
+  int k[LT<D>::NI];
+};
+
+template <int D, bool PV>
+struct LState {
+  f32x16 o[2][LT<D>::VT];
+  float m[2];
+  float l[2];
+};
+
+// Keys of the NI entries this lane copies (entries NI*g + 0..NI-1 of the step).
+template <int D, bool GATHER>
+__device__ __forceinline__ void lkeys(LKeys<D>& kk, __amdgpu_buffer_rsrc_t ridx, int t0, int ebase) {
+  using L = LT<D>;
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int c = 0; c < L::NI / 4; ++c) {
+      const u32x4 w = bload128(ridx, (uint32_t)(t0 + ebase + 4 * c) * 4u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kk.k[4 * c + j] = (int)w[j];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::NI; ++i) kk.k[i] = t0 + ebase + i;
+  }
+}
+
+// Start the copies of one step's K (and V) rows into a stage.  A key of -1 (a
+// padding entry) or past the sequence gives an offset beyond the buffer, which
+// the buffer unit answers with zeros; those entries are masked anyway.
+template <int D, bool PV>
+__device__ __forceinline__ void ldma(LDSP char* stage, const LKeys<D>& kk, __amdgpu_buffer_rsrc_t rk,
+                                     __amdgpu_buffer_rsrc_t rv, uint32_t goff) {
+  using L = LT<D>;
+#pragma unroll
+  for (int i = 0; i < L::NI; ++i) {
+    const uint32_t vo = (uint32_t)kk.k[i] * (uint32_t)L::ROWB + goff;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDSP void*)(stage + i * L::BLK), 16, vo, 0, 0, 0);
+    if constexpr (PV)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDSP void*)(stage + L::TILE + i * L::BLK), 16, vo, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void lkread(u32x4 (&ka)[LT<D>::KCH], const LDSP char* stage, const int (&kaddr)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < LT<D>::KCH; ++ks) ka[ks] = *(const LDSP u32x4*)(stage + kaddr[ks & 1] + 64 * (ks >> 1));
+}
+
+template <int D>
+__device__ __forceinline__ void lqk(f32x16 (&s)[2], const u32x4 (&ka)[LT<D>::KCH], const u32x4 (&q)[2][LT<D>::KCH]) {
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < LT<D>::KCH; ++ks)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) s[nt] = mfma_bf16(as_bf16x8(ka[ks]), as_bf16x8(q[nt][ks]), s[nt]);
+}
+
+__device__ __forceinline__ void lmask(f32x16 (&s)[2], int t0, int nkeys, int hf) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (t0 + 8 * (r >> 2) + 4 * hf + (r & 3) >= nkeys) s[nt][r] = -INFINITY;
+}
+
+template <int D, bool PV, bool EXACT_SUM>
+__device__ __forceinline__ void lprobs(LState<D, PV>& st, f32x16 (&s)[2], uint32_t (&pk)[2][8], float c) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float moff = st.m[nt];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[nt][r] = fast_exp2(__builtin_fmaf(s[nt][r], c, -moff));
+    if constexpr (PV) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[nt][i] = pack_bf16x2(s[nt][2 * i], s[nt][2 * i + 1]);
+    }
+    if constexpr (EXACT_SUM) {
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls += s[nt][r];
+      st.l[nt] += ls;
+    } else {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      float ls = st.l[nt];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[nt][i]), one, ls, false);
+      st.l[nt] = ls;
+    }
+  }
+}
+
+// V operands of one step: for key chunk kc and output tile n, two transposing
+// reads give a lane dimension 32*n + lane%32 of the 8 keys its k-slots name.
+template <int D>
+__device__ __forceinline__ void lvread(bf16x8 (&vb)[2][LT<D>::VT], const LDSP char* stage, const int (&vaddr)[2][2]) {
+  using L = LT<D>;
+  typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+  const LDSP char* vt = stage + L::TILE;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int n = 0; n < L::VT; ++n) {
+      const bf4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + vaddr[kc][0] + 64 * n));
+      const bf4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + vaddr[kc][1] + 64 * n));
+      vb[kc][n] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void lpv(LState<D, true>& st, const uint32_t (&pk)[2][8], const bf16x8 (&vb)[2][LT<D>::VT]) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    bf16x8 pa[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pk[nt][4 * kc + i];
+      pa[nt] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int n = 0; n < LT<D>::VT; ++n)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) st.o[nt][n] = mfma_bf16(pa[nt], vb[kc][n], st.o[nt][n]);
+  }
+}
+
+// Per-lane context of the LDS path.
+template <int D>
+struct LCtx {
+  __amdgpu_buffer_rsrc_t rk, rv, ridx;
+  int nkeys, hf, ebase;
+  uint32_t goff;
+  int kaddr[2];
+  int vaddr[2][2];
+  float c;
+};
+
+// One step on stage `cur`.  DMA_NEXT: start the copies of step it+1 into `nxt`
+// (keys in kn) and load the keys of step it+2 into kn; FIRST: fix the offsets
+// from this step's maxima; LAST: mask entries past the key count.
+template <int D, bool GATHER, bool PV, bool FIRST, bool LAST, bool DMA_NEXT>
+__device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
+                                      const LDSP char* cur, LDSP char* nxt, LKeys<D>& kn, int it) {
+  constexpr bool EXACT = !GATHER || !PV;
+  // Phases are kept apart with scheduling barriers: the operand reads go out
+  // early as a batch (the default schedule issues each LDS read right before its
+  // MFMA and waits for it), and the copies of the next step overlap the QK
+  // product.
+  u32x4 ka[LT<D>::KCH];
+  lkread<D>(ka, cur, x.kaddr);
+  if constexpr (DMA_NEXT) {
+    ldma<D, PV>(nxt, kn, x.rk, x.rv, x.goff);
+    lkeys<D, GATHER>(kn, x.ridx, (it + 2) * 32, x.ebase);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s[2];
+  uint32_t pk[2][8];
+  lqk<D>(s, ka, q);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 vb[2][LT<D>::VT];
+  if constexpr (PV) lvread<D>(vb, cur, x.vaddr);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LAST) lmask(s, it * 32, x.nkeys, x.hf);
+  if constexpr (FIRST) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = s[nt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+      st.m[nt] = pair_max(mx) * x.c + kMargin;
+    }
+  }
+  lprobs<D, PV, EXACT>(st, s, pk, x.c);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PV) lpv<D>(st, pk, vb);
+}
+
+// The whole key list: first step, a branch-free middle of step pairs on the two
+// stages (no masking; the key prefetch may read past the list, which returns
+// zeros or unused entries), then at most one more middle step and the masked
+// last step.
+template <int D, bool GATHER, bool PV>
+__device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
+                                      LDSP char* s0, LDSP char* s1) {
+  const int nsteps = (x.nkeys + 31) >> 5;
+  LKeys<D> kn;
+  lkeys<D, GATHER>(kn, x.ridx, 0, x.ebase);
+  ldma<D, PV>(s0, kn, x.rk, x.rv, x.goff);
+  lkeys<D, GATHER>(kn, x.ridx, 32, x.ebase);
+  if (nsteps == 1) {
+    lstep<D, GATHER, PV, true, true, false>(st, x, q, s0, s1, kn, 0);
+    return;
+  }
+  lstep<D, GATHER, PV, true, false, true>(st, x, q, s0, s1, kn, 0);
+  int it = 1;
+  for (; it + 2 < nsteps; it += 2) {
+    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, kn, it);
+    lstep<D, GATHER, PV, false, false, true>(st, x, q, s0, s1, kn, it + 1);
+  }
+  // it is odd: stage s1 holds step it
+  if (it + 1 < nsteps) {
+    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, kn, it);
+    lstep<D, GATHER, PV, false, true, false>(st, x, q, s0, s1, kn, it + 1);
+  } else {
+    lstep<D, GATHER, PV, false, true, false>(st, x, q, s1, s0, kn, it);
+  }
+}
+
+// Normalisation, statistics and epilogue of the LDS path.  O goes through LDS
+// (fp32, one half of the group at a time) so that every lane stores 16
+// contiguous bytes of one output row, and the residual is added in fp32 before
+// the single rounding to bf16.
+template <int D, int EPI, bool PV>
+__device__ __forceinline__ void lfinish(const LState<D, PV>& st, const AttnArgs& a, int h, const int (&tokq)[2],
+                                        const bool (&qvalid)[2], int lane, LDSP char* buf) {
+  using L = LT<D>;
+  const int N = a.N, hf = lane >> 5, lm = lane & 31;
+  float inv[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float lt = pair_sum(st.l[nt]);
+    inv[nt] = 1.0f / lt;
+    if (hf == 0 && qvalid[nt]) {
+      const size_t ri = (size_t)h * N + tokq[nt];
+      if (a.stats) a.stats[ri] = make_float2(st.m[nt], inv[nt]);
+      if (a.lse) a.lse[ri] = (st.m[nt] + __log2f(lt)) * kLn2;
+    }
+  }
+  if constexpr (PV) {
+    constexpr int LPO = D / 8;        // lanes per output row (8 dims each)
+    constexpr int RPO = 64 / LPO;     // rows per pass
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 8 * (r >> 2) + 4 * hf + (r & 3);
+        const float ir = lane_read(inv[nt], qi);
+#pragma unroll
+        for (int n = 0; n < L::VT; ++n)
+          *(LDSP float*)(buf + qi * L::OPITCH + (32 * n + lm) * 4) = st.o[nt][n][r] * ir;
+      }
+      const int tok_l = tokq[nt], ok_l = qvalid[nt] ? 1 : 0;
+      const int ch = lane % LPO;
+#pragma unroll
+      for (int p = 0; p < 32 / RPO; ++p) {
+        const int qi = p * RPO + lane / LPO;
+        const LDSP char* src = buf + qi * L::OPITCH + ch * 32;
+        const f32x4 v0 = *(const LDSP f32x4*)src;
+        const f32x4 v1 = *(const LDSP f32x4*)(src + 16);
+        const int tok = lane_read_i(tok_l, qi);
+        const int ok = lane_read_i(ok_l, qi);
+        float vals[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        if (ok) {
+          const size_t base = ((size_t)h * N + tok) * D + (size_t)ch * 8;
+          if constexpr (EPI != EPI_PLAIN) {
+            const u32x4 rw = *(const u32x4*)((const __bf16*)a.rin + base);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float r0 = bf16lo(rw[i]), r1 = bf16hi(rw[i]);
+              vals[2 * i] = EPI == EPI_ADD ? vals[2 * i] + r0 : r0 - vals[2 * i];
+              vals[2 * i + 1] = EPI == EPI_ADD ? vals[2 * i + 1] + r1 : r1 - vals[2 * i + 1];
+            }
+          }
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(vals[2 * i], vals[2 * i + 1]);
+          *(u32x4*)((__bf16*)a.o + base) = w;
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool GATHER, int EPI, bool PV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_lds_kernel(AttnArgs a) {
+  using L = LT<D>;
+  __shared__ __attribute__((aligned(16))) char stage0[4][L::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[4][L::STAGE];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int hf = lane >> 5, lm = lane & 31;
+  const int items = a.H * a.G;
+  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
+  if (blk < 0) return;
+  const int item = blk * 4 + wid;
+  if (item >= items) return;  // waves are independent: no block-level synchronisation
+  const int h = item / a.G, g = item - h * a.G;
+  const int N = a.N;
+  const size_t head_off = (size_t)h * N * L::ROWB;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * L::ROWB);
+  const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
+  LDSP char* s0 = (LDSP char*)&stage0[wid][0];
+  LDSP char* s1 = (LDSP char*)&stage1[wid][0];
+
+  LCtx<D> x;
+  x.rk = make_rsrc((const char*)a.k + head_off, head_bytes);
+  x.rv = make_rsrc((const char*)a.v + head_off, head_bytes);
+  x.ridx = GATHER ? make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad, (uint32_t)a.kpad * 4u) : make_rsrc(nullptr, 0);
+  x.nkeys = a.nkeys;
+  x.hf = hf;
+  x.c = a.c;
+  {
+    const int gd = lane / L::LPR, cj = lane % L::LPR;
+    x.goff = 16u * (uint32_t)(cj ^ L::swz(gd));
+    x.ebase = L::NI * gd;
+    // K operand: lane row m = lm (entry m), chunk 2*ks + hf
+#pragma unroll
+    for (int v = 0; v < 2; ++v) x.kaddr[v] = L::off(lm, 2 * v + hf);
+    // V operand (transposing read): lane i of its 16-lane group supplies the
+    // address of 4 dims of one key; see lpv for the resulting layout
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int sr = 0; sr < 2; ++sr) {
+        const int e = 16 * kc + 8 * sr + 4 * (g16 >> 1) + (i16 >> 2);
+        const int xch = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+        x.vaddr[kc][sr] = L::off(e, xch) + 8 * (i16 & 1);
+      }
+  }
+
+  int tokq[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int slot = g * 64 + lm + 32 * nt;
+    qvalid[nt] = slot < N;
+    tokq[nt] = qvalid[nt] ? (a.perm ? a.perm[(size_t)h * N + slot] : slot) : 0;
+    if (tokq[nt] < 0 || tokq[nt] >= N) {
+      qvalid[nt] = false;
+      tokq[nt] = 0;
+    }
+  }
+  u32x4 q[2][L::KCH];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint32_t qb = (uint32_t)tokq[nt] * L::ROWB + 16u * hf;
+#pragma unroll
+    for (int c = 0; c < L::KCH; ++c) q[nt][c] = bload128(rq, qb + c * 32);
+  }
+
+  // Stages start zeroed: a padding entry's copy may leave its slot untouched,
+  // and a masked probability times a stale non-finite value would poison O.
+  for (int o = lane * 16; o < L::STAGE; o += 64 * 16) {
+    *(LDSP u32x4*)(s0 + o) = u32x4{0, 0, 0, 0};
+    *(LDSP u32x4*)(s1 + o) = u32x4{0, 0, 0, 0};
+  }
+  // The copies below land in LDS through the texture path, not in order behind
+  // these stores: the stores must be done before the first copy is issued.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  LState<D, PV> st;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    st.m[nt] = 0.0f;
+    st.l[nt] = 0.0f;
+    if constexpr (PV) {
+#pragma unroll
+      for (int n = 0; n < L::VT; ++n) st.o[nt][n] = f32x16{};
+    }
+  }
+  if (x.nkeys > 0) lpass<D, GATHER, PV>(st, x, q, s0, s1);
+
+  const bool ok = __builtin_isfinite(st.l[0]) && __builtin_isfinite(st.l[1]);
+  if (__builtin_amdgcn_ballot_w64(!ok)) {
+    // a logit far above its query's first-tile maximum overflowed the fixed
+    // offset: redo the group with the online pass (direct global loads)
+    Ctx<__bf16, D, GATHER> xo;
+    xo.rk = x.rk;
+    xo.rv = x.rv;
+    xo.ridx = x.ridx;
+    xo.nkeys = x.nkeys;
+    xo.lm = lm;
+    xo.hf = hf;
+    xo.c = x.c;
+    State<__bf16, D, PV> so;
+    state_init<__bf16, D, PV>(so);
+    pass_online<__bf16, D, GATHER, PV>(so, xo, q);
+    finish<__bf16, D, EPI, PV>(so, a, h, g, tokq, qvalid, lm, hf);
+  } else {
+    lfinish<D, EPI, PV>(st, a, h, tokq, qvalid, lane, s0);
+  }
+}
+
+template <int D, bool GATHER, int EPI, bool PV>
+hipError_t launch_lds(const AttnArgs& a, hipStream_t s) {
+  const int items = a.H * a.G;
+  const int blocks = xcd_grid((items + 3) / 4);
+  hipLaunchKernelGGL((attn_lds_kernel<D, GATHER, EPI, PV>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool GATHER, int EPI, bool PV>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int items = a.H * a.G;
@@ -562,15 +1003,27 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_d(const AttnArgs& a, bool gather, int epi, bool pv, hipStream_t s) {
-  if (!pv) return gather ? launch_t<T, D, true, EPI_PLAIN, false>(a, s) : launch_t<T, D, false, EPI_PLAIN, false>(a, s);
-  if (gather) {
-    switch (epi) {
-      case EPI_ADD: return launch_t<T, D, true, EPI_ADD, true>(a, s);
-      case EPI_RESID: return launch_t<T, D, true, EPI_RESID, true>(a, s);
-      default: return launch_t<T, D, true, EPI_PLAIN, true>(a, s);
+  if constexpr (std::is_same<T, __bf16>::value) {
+    if (!pv) return gather ? launch_lds<D, true, EPI_PLAIN, false>(a, s) : launch_lds<D, false, EPI_PLAIN, false>(a, s);
+    if (gather) {
+      switch (epi) {
+        case EPI_ADD: return launch_lds<D, true, EPI_ADD, true>(a, s);
+        case EPI_RESID: return launch_lds<D, true, EPI_RESID, true>(a, s);
+        default: return launch_lds<D, true, EPI_PLAIN, true>(a, s);
+      }
     }
+    return launch_lds<D, false, EPI_PLAIN, true>(a, s);
+  } else {
+    if (!pv) return gather ? launch_t<T, D, true, EPI_PLAIN, false>(a, s) : launch_t<T, D, false, EPI_PLAIN, false>(a, s);
+    if (gather) {
+      switch (epi) {
+        case EPI_ADD: return launch_t<T, D, true, EPI_ADD, true>(a, s);
+        case EPI_RESID: return launch_t<T, D, true, EPI_RESID, true>(a, s);
+        default: return launch_t<T, D, true, EPI_PLAIN, true>(a, s);
+      }
+    }
+    return launch_t<T, D, false, EPI_PLAIN, true>(a, s);
   }
-  return launch_t<T, D, false, EPI_PLAIN, true>(a, s);
 }
 
 }  // namespace
