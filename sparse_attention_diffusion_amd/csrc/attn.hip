@@ -392,13 +392,32 @@ __device__ __forceinline__ void pass_fixed(State<T, D, PV>& st, const Ctx<T, D, 
   }
 }
 
+// Q operand of the group: lane half hf of query column lm + 32*nt holds the
+// dims of its half of every k-chunk.
+template <typename T, int D>
+__device__ __forceinline__ void load_q(__amdgpu_buffer_rsrc_t rq, const int (&tokq)[2], int hf,
+                                       u32x4 (&q)[2][Tile<T, D>::KCH]) {
+  using TL = Tile<T, D>;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
+#pragma unroll
+    for (int c = 0; c < TL::KCH; ++c) q[nt][c] = bload128(rq, qb + c * TL::KSTRIDE);
+  }
+}
+
 // Online pass with a running maximum and lazy rescaling (the offset moves only
 // when the maximum grows by more than 2^8).  Used only for groups whose
 // fixed-offset pass overflowed.
 template <typename T, int D, bool GATHER, bool PV>
 __device__ __attribute__((noinline)) void pass_online(State<T, D, PV>& st, const Ctx<T, D, GATHER>& x,
-                                                      const u32x4 (&q)[2][Tile<T, D>::KCH]) {
+                                                      __amdgpu_buffer_rsrc_t rq, int tok0, int tok1) {
+  // Q is reloaded here rather than passed in: an array argument of a
+  // non-inlined call would force the caller's copy into scratch memory.
   constexpr bool EXACT = !GATHER;
+  const int tokq[2] = {tok0, tok1};
+  u32x4 q[2][Tile<T, D>::KCH];
+  load_q<T, D>(rq, tokq, x.hf, q);
   Idx ix;
   KV<T, D> b;
   const int nsteps = (x.nkeys + 31) >> 5;
@@ -531,12 +550,7 @@ void attn_kernel(AttnArgs a) {
     }
   }
   u32x4 q[2][TL::KCH];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint32_t qb = (uint32_t)tokq[nt] * TL::ROWB + TL::khalf_off(hf);
-#pragma unroll
-    for (int c = 0; c < TL::KCH; ++c) q[nt][c] = bload128(rq, qb + c * TL::KSTRIDE);
-  }
+  load_q<T, D>(rq, tokq, hf, q);
 
   State<T, D, PV> st;
   state_init<T, D, PV>(st);
@@ -545,7 +559,7 @@ void attn_kernel(AttnArgs a) {
   if (__builtin_amdgcn_ballot_w64(!ok)) {
     State<T, D, PV> so;
     state_init<T, D, PV>(so);
-    pass_online<T, D, GATHER, PV>(so, x, q);
+    pass_online<T, D, GATHER, PV>(so, x, rq, tokq[0], tokq[1]);
     finish<T, D, EPI, PV>(so, a, h, g, tokq, qvalid, lm, hf);
   } else {
     finish<T, D, EPI, PV>(st, a, h, g, tokq, qvalid, lm, hf);
@@ -738,6 +752,16 @@ struct LCtx {
   float c;
 };
 
+// Explicit wait on the vector memory counter.  The compiler's own tracking of
+// the LDS copies is not relied on: across a loop back-edge it has been seen to
+// drop the wait a stage read needs.  Loads retire in order, so vmcnt(n) means
+// "everything but the last n vector memory instructions has landed".
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // One step on stage `cur`.  DMA_NEXT: start the copies of step it+1 into `nxt`
 // (keys in kn) and load the keys of step it+2 into kn; FIRST: fix the offsets
 // from this step's maxima; LAST: mask entries past the key count.
@@ -749,6 +773,9 @@ __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const
   // early as a batch (the default schedule issues each LDS read right before its
   // MFMA and waits for it), and the copies of the next step overlap the QK
   // product.
+  // the copies of this step and the keys of the next were the last vector
+  // memory instructions issued: all of them are needed now
+  wait_vm<0>();
   u32x4 ka[LT<D>::KCH];
   lkread<D>(ka, cur, x.kaddr);
   if constexpr (DMA_NEXT) {
@@ -978,7 +1005,7 @@ void attn_lds_kernel(AttnArgs a) {
     xo.c = x.c;
     State<__bf16, D, PV> so;
     state_init<__bf16, D, PV>(so);
-    pass_online<__bf16, D, GATHER, PV>(so, xo, q);
+    pass_online<__bf16, D, GATHER, PV>(so, xo, rq, tokq[0], tokq[1]);
     finish<__bf16, D, EPI, PV>(so, a, h, g, tokq, qvalid, lm, hf);
   } else {
     lfinish<D, EPI, PV>(st, a, h, tokq, qvalid, lane, s0);
