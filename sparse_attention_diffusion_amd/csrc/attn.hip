@@ -23,6 +23,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ldstile.hpp"
 
 namespace mcs {
 
@@ -590,24 +591,6 @@ void attn_kernel(AttnArgs a) {
 //   half hf holds entry 8*(r/4) + 4*hf + r%4.
 // Two stages (separate LDS arrays, so the compiler's wait counting can tell the
 // in-flight copy of step i+1 from the one step i reads) alternate.
-template <int D>
-struct LT {
-  static constexpr int ROWB = D * 2;
-  static constexpr int LPR = ROWB / 16;   // lanes per row in a DMA
-  static constexpr int RPI = 64 / LPR;    // rows per DMA instruction
-  static constexpr int NI = 32 / RPI;     // DMA instructions per tile
-  static constexpr int BLK = 1024 + 32;
-  static constexpr int TILE = NI * BLK;
-  static constexpr int KCH = D / 16;      // QK k-chunks of 16 dims
-  static constexpr int VT = D / 32;       // PV output tiles of 32 dims
-  // epilogue: half of the group's O (32 queries, fp32) with a 16-byte row skew
-  static constexpr int OPITCH = D * 4 + 16;
-  static constexpr int STAGE = (2 * TILE > 32 * OPITCH) ? 2 * TILE : 32 * OPITCH;
-  __device__ static int swz(int g) { return (g * ROWB / 256) & 3; }
-  __device__ static int off(int e, int x) { return (e % NI) * BLK + (e / NI) * ROWB + 16 * (x ^ swz(e / NI)); }
-};
-
-#define LDSP __attribute__((address_space(3)))
 
 template <int D>
 struct LKeys {
@@ -752,15 +735,6 @@ struct LCtx {
   float c;
 };
 
-// Explicit wait on the vector memory counter.  The compiler's own tracking of
-// the LDS copies is not relied on: across a loop back-edge it has been seen to
-// drop the wait a stage read needs.  Loads retire in order, so vmcnt(n) means
-// "everything but the last n vector memory instructions has landed".
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // One step on stage `cur`.  DMA_NEXT: start the copies of step it+1 into `nxt`
 // (keys in kn) and load the keys of step it+2 into kn; FIRST: fix the offsets

@@ -18,6 +18,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ldstile.hpp"
 
 namespace mcs {
 
@@ -357,6 +358,156 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, w);
 }
 
+// bf16 pass 2 with K staged through LDS.  Every group scans all keys in the
+// same order, so the four waves of a block take four consecutive groups of one
+// head and share each K tile: every wave issues a quarter of the tile's copies
+// and one block barrier per step separates "copies landed / previous tile
+// consumed" from the reads.  This cuts the address work of the K fetches by
+// 16x (quad-contiguous copies, a quarter each) and the L2 traffic by 4x.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void group_mass_lds_kernel(MassArgs a) {
+  using L = LT<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int hf = lane >> 5, lm = lane & 31;
+  const int gb = (a.G + 3) >> 2;
+  const int blk = xcd_remap(blockIdx.x, a.hcount * gb, a.xcd_chunk);
+  if (blk < 0) return;  // the whole block
+  const int hl = blk / gb;
+  const int g = (blk - hl * gb) * 4 + wid;
+  const bool active = g < a.G;  // a wave past the last group only helps copy
+  WaveLds* w = (WaveLds*)smem + wid;
+  LDSP char* s0 = (LDSP char*)(smem + 4 * sizeof(WaveLds));
+  LDSP char* s1 = s0 + L::TILE;
+  const int h = a.h0 + hl;
+  const int N = a.N;
+  const size_t head_off = (size_t)h * N * L::ROWB;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * L::ROWB);
+  const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
+  const auto rk = make_rsrc((const char*)a.k + head_off, head_bytes);
+  for (int j = lane; j < kHistBins; j += 64) w->hist[j] = 0;
+
+  // Query rows of this group: lane lm holds queries lm and lm + 32 (A operand).
+  int tokq[2];
+  bool qvalid[2];
+  u32x4 q[2][L::KCH];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int slot = g * 64 + lm + 32 * nt;
+    qvalid[nt] = active && slot < N;
+    tokq[nt] = qvalid[nt] ? a.perm[(size_t)h * N + slot] : 0;
+    if (tokq[nt] < 0 || tokq[nt] >= N) {
+      qvalid[nt] = false;
+      tokq[nt] = 0;
+    }
+    const uint32_t qb = (uint32_t)tokq[nt] * L::ROWB + 16u * hf;
+#pragma unroll
+    for (int c = 0; c < L::KCH; ++c) q[nt][c] = bload128(rq, qb + c * 32);
+  }
+  float rm[2][16], rw[2][16];
+  float my_m[2], my_w[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if (!qvalid[nt]) {
+      my_m[nt] = INFINITY;
+      my_w[nt] = 0.0f;
+    } else if (a.stats) {
+      const float2 st = a.stats[(size_t)h * N + tokq[nt]];
+      my_m[nt] = st.x;
+      my_w[nt] = st.y;
+    } else {
+      my_m[nt] = a.lse[(size_t)h * N + tokq[nt]] * kLog2e;
+      my_w[nt] = 1.0f;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int src = 8 * (r >> 2) + 4 * hf + (r & 3);
+      rm[nt][r] = lane_read(my_m[nt], src);
+      rw[nt][r] = lane_read(my_w[nt], src);
+    }
+
+  float* out = a.mass + ((size_t)hl * a.G + (active ? g : 0)) * (size_t)a.ldm;
+  const float c = a.c;
+  const int nsteps = (N + 31) >> 5;
+  const uint32_t goff = tile_goff<D>(lane);
+  const int ebase = tile_ebase<D>(lane);
+  int kaddr[2];
+  tile_kaddr<D>(kaddr, lm, hf);
+  constexpr int NC = L::NI / 4;
+
+  auto qk = [&](f32x16 (&s)[2], const LDSP char* tile) {
+    u32x4 kb[L::KCH];
+    tile_kread<D>(kb, tile, kaddr);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      s[nt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < L::KCH; ++ks) s[nt] = mfma_bf16(as_bf16x8(q[nt][ks]), as_bf16x8(kb[ks]), s[nt]);
+    }
+  };
+  auto reduce_store = [&](const f32x16 (&s)[2], int t0) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc = __builtin_fmaf(fast_exp2(__builtin_fmaf(s[nt][r], c, -rm[nt][r])), rw[nt][r], acc);
+    acc = pair_sum(acc);
+    if (active && hf == 0 && t0 + lm < N) {
+      out[t0 + lm] = acc;
+      atomicAdd(&w->hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
+    }
+  };
+  // Iteration i: barrier (every wave's copy of K(i+1) landed, every wave done
+  // with K(i)'s stage), copy K(i+2) into that stage, QK of step i+1, then the
+  // exponentials of step i (they overlap the MFMAs).  K(j) lives in stage j % 2.
+  auto iter = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], LDSP char* sp, LDSP char* sq, int i) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<0>();
+    __syncthreads();
+    if (i + 2 < nsteps) tile_copy_dense<D, NC>(sp, rk, i + 2, ebase, goff, wid * NC);
+    __builtin_amdgcn_sched_barrier(0);
+    qk(sn, sq);
+    reduce_store(sc, i * 32);
+  };
+  f32x16 sa[2], sb[2];
+  tile_copy_dense<D, NC>(s0, rk, 0, ebase, goff, wid * NC);
+  if (nsteps > 1) tile_copy_dense<D, NC>(s1, rk, 1, ebase, goff, wid * NC);
+  wait_vm<0>();
+  __syncthreads();
+  qk(sa, s0);
+  int it = 0;
+  for (; it + 2 < nsteps; it += 2) {
+    iter(sa, sb, s0, s1, it);
+    iter(sb, sa, s1, s0, it + 1);
+  }
+  if (it + 1 < nsteps) {
+    iter(sa, sb, s0, s1, it);
+    reduce_store(sb, (it + 1) * 32);
+  } else {
+    reduce_store(sa, it * 32);
+  }
+  if (!active) return;  // no block-level synchronisation below
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, w);
+}
+
+template <int D>
+hipError_t launch_mass_lds(const MassArgs& a, hipStream_t s) {
+  const int blocks = xcd_grid(a.hcount * ((a.G + 3) / 4));
+  const size_t lds = 4 * sizeof(WaveLds) + 2 * LT<D>::TILE;
+  hipError_t e = hipFuncSetAttribute((const void*)group_mass_lds_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((group_mass_lds_kernel<D>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   const int items = a.hcount * a.G;
@@ -372,7 +523,7 @@ hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s) {
-  if (dtype == DT_BF16) return head_dim == 128 ? launch_mass_t<__bf16, 128>(a, s) : launch_mass_t<__bf16, 64>(a, s);
+  if (dtype == DT_BF16) return head_dim == 128 ? launch_mass_lds<128>(a, s) : launch_mass_lds<64>(a, s);
   return head_dim == 128 ? launch_mass_t<float, 128>(a, s) : launch_mass_t<float, 64>(a, s);
 }
 
