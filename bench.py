@@ -32,6 +32,38 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E (published)
 
+# Sources of the gather-sparse kernel: the committed counter summary applies only
+# while these are byte-identical to the ones it was taken from.
+KERNEL_SOURCES = ("sparse_attention_diffusion_amd/csrc/attn.hip", "sparse_attention_diffusion_amd/csrc/ldstile.hpp",
+                  "sparse_attention_diffusion_amd/csrc/common.hpp", "sparse_attention_diffusion_amd/csrc/kernels.hpp")
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str, density: float):
+    """HBM bytes per launch of the gather-sparse kernel from the committed
+    FETCH_SIZE / WRITE_SIZE summary (calibrated against a copy of known size), or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_gather_sparse_{workload}_density{density:g}.md")
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("sources_sha256") == sources_sha256():
+                        return int(rec["bytes_per_launch"])
+                    return None
+    except OSError:
+        return None
+    return None
+
 
 def pct_of_ideal(speedup: float, density: float) -> float:
     """Fraction of the ideal 1/density speedup (4.79x at density 0.2 is 0.958)."""
@@ -109,6 +141,8 @@ def main():
     ap.add_argument("--density", type=float, default=0.2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sdpa", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="copy 1 GiB once before the workload (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MC-Sparse hot path is built and timed on a single MI355X "
@@ -127,6 +161,12 @@ def main():
     kk = wl.topk(args.density)
     print(f"[bench] {wl.name}: N={n} H={h} D={d} {wl.dtype} C={wl.group} density={args.density} K={kk}",
           file=sys.stderr, flush=True)
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     q, k, v = W.make_qkv_torch(wl, dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -193,7 +233,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.grid[0]}x{wl.grid[1]}x{wl.grid[2]} grid, N={n}, H={h}, D={d}, "
                                f"bf16, C={wl.group}, density={args.density}, K={kk}",
-                   "global_batch": 1, "seq_len": n, "parallelism": "single-gpu"},
+                   "tokens": n, "heads": h, "head_dim": d, "group": wl.group, "density": args.density, "topk": kk},
         "pct_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "x_vs_dense": round(speedup, 3),
         "pct_of_ideal": round(100.0 * pct_of_ideal(speedup, args.density), 1),
@@ -201,7 +241,8 @@ def main():
         "stage_ms": {key: round(val, 3) for key, val in ms.items()},
         "torch_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": committed_traffic(wl.name, args.density)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, cache["perm"], cache["idx"], kk, 1.0 / d ** 0.5)
