@@ -51,6 +51,14 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Block barrier without the memory fence of __syncthreads(): that fence waits for
+// every outstanding global store (vmcnt(0)), which would expose a store's write
+// latency at every step.  Shared tiles need no fence: each wave waits for its
+// own copies (wait_vm) before the barrier, and its reads of the previous tile
+// were consumed before it arrives.  The "memory" clobber keeps the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Lane constants of the tile copies: the byte offset of this lane's 16-byte
 // chunk within a row, and the first step entry this lane copies.
 template <int D>

@@ -431,6 +431,11 @@ void group_mass_lds_kernel(MassArgs a) {
     }
 
   float* out = a.mass + ((size_t)hl * a.G + (active ? g : 0)) * (size_t)a.ldm;
+  // Mass stores go through a buffer descriptor so that every wave issues exactly
+  // one store instruction per step (lanes with nothing to store, and every lane
+  // of a wave past the last group, aim past the range and are dropped): the
+  // per-step wait below then knows that exactly one store follows the copies.
+  const auto rout = make_rsrc(out, active ? (uint32_t)a.ldm * 4u : 0u);
   const float c = a.c;
   const int nsteps = (N + 31) >> 5;
   const uint32_t goff = tile_goff<D>(lane);
@@ -457,18 +462,22 @@ void group_mass_lds_kernel(MassArgs a) {
       for (int r = 0; r < 16; ++r)
         acc = __builtin_fmaf(fast_exp2(__builtin_fmaf(s[nt][r], c, -rm[nt][r])), rw[nt][r], acc);
     acc = pair_sum(acc);
-    if (active && hf == 0 && t0 + lm < N) {
-      out[t0 + lm] = acc;
-      atomicAdd(&w->hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
-    }
+    const bool keep = active && hf == 0 && t0 + lm < N;
+    uint32_t soff = keep ? (uint32_t)(t0 + lm) * 4u : 0xfffffff0u;
+    asm volatile("" : "+v"(soff));  // opaque: keeps the store out of the branch on `keep`
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rout, soff, 0, 0);
+    if (keep) atomicAdd(&w->hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
   };
   // Iteration i: barrier (every wave's copy of K(i+1) landed, every wave done
   // with K(i)'s stage), copy K(i+2) into that stage, QK of step i+1, then the
   // exponentials of step i (they overlap the MFMAs).  K(j) lives in stage j % 2.
   auto iter = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], LDSP char* sp, LDSP char* sq, int i) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<0>();
-    __syncthreads();
+    // this wave's copies of K(i+1) came before the one mass store of step i-1:
+    // everything but that store must have landed (a store's completion is not
+    // needed here, and waiting for it would expose the write latency every step)
+    wait_vm<1>();
+    block_barrier();
     if (i + 2 < nsteps) tile_copy_dense<D, NC>(sp, rk, i + 2, ebase, goff, wid * NC);
     __builtin_amdgcn_sched_barrier(0);
     qk(sn, sq);
@@ -478,7 +487,7 @@ void group_mass_lds_kernel(MassArgs a) {
   tile_copy_dense<D, NC>(s0, rk, 0, ebase, goff, wid * NC);
   if (nsteps > 1) tile_copy_dense<D, NC>(s1, rk, 1, ebase, goff, wid * NC);
   wait_vm<0>();
-  __syncthreads();
+  block_barrier();
   qk(sa, s0);
   int it = 0;
   for (; it + 2 < nsteps; it += 2) {
