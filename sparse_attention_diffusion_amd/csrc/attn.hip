@@ -741,21 +741,26 @@ struct LCtx {
 // from this step's maxima; LAST: mask entries past the key count.
 template <int D, bool GATHER, bool PV, bool FIRST, bool LAST, bool DMA_NEXT>
 __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
-                                      const LDSP char* cur, LDSP char* nxt, LKeys<D>& kn, int it) {
+                                      const LDSP char* cur, LDSP char* nxt, const LKeys<D>& kcur, LKeys<D>& knext,
+                                      int it) {
   constexpr bool EXACT = !GATHER || !PV;
-  // Phases are kept apart with scheduling barriers: the operand reads go out
-  // early as a batch (the default schedule issues each LDS read right before its
-  // MFMA and waits for it), and the copies of the next step overlap the QK
-  // product.
-  // the copies of this step and the keys of the next were the last vector
-  // memory instructions issued: all of them are needed now
-  wait_vm<0>();
+  constexpr int NKL = GATHER ? LT<D>::NI / 4 : 0;        // key loads per step
+  constexpr int NDMA = (PV ? 2 : 1) * LT<D>::NI;         // copy instructions per step
+  // The copies of step it+1 (keys in kcur) and the key load of step it+2 go out
+  // before waiting for this step's copies, so two steps of rows are in flight
+  // while the wave waits: the gathers are bound by the cache hierarchy's
+  // latency, and one step in flight per wave is too little to cover it.
+  if constexpr (DMA_NEXT) {
+    lkeys<D, GATHER>(knext, x.ridx, (it + 2) * 32, x.ebase);
+    ldma<D, PV>(nxt, kcur, x.rk, x.rv, x.goff);
+    // this step's copies landed once at most those two batches remain
+    wait_vm<NKL + NDMA>();
+  } else {
+    wait_vm<0>();
+  }
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 ka[LT<D>::KCH];
   lkread<D>(ka, cur, x.kaddr);
-  if constexpr (DMA_NEXT) {
-    ldma<D, PV>(nxt, kn, x.rk, x.rv, x.goff);
-    lkeys<D, GATHER>(kn, x.ridx, (it + 2) * 32, x.ebase);
-  }
   __builtin_amdgcn_sched_barrier(0);
   f32x16 s[2];
   uint32_t pk[2][8];
@@ -782,31 +787,32 @@ __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const
 // The whole key list: first step, a branch-free middle of step pairs on the two
 // stages (no masking; the key prefetch may read past the list, which returns
 // zeros or unused entries), then at most one more middle step and the masked
-// last step.
+// last step.  Step j's rows live in stage j % 2; the keys of steps alternate
+// between ka and kb the same way.
 template <int D, bool GATHER, bool PV>
 __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
                                       LDSP char* s0, LDSP char* s1) {
   const int nsteps = (x.nkeys + 31) >> 5;
-  LKeys<D> kn;
-  lkeys<D, GATHER>(kn, x.ridx, 0, x.ebase);
-  ldma<D, PV>(s0, kn, x.rk, x.rv, x.goff);
-  lkeys<D, GATHER>(kn, x.ridx, 32, x.ebase);
+  LKeys<D> ka, kb;
+  lkeys<D, GATHER>(ka, x.ridx, 0, x.ebase);
+  ldma<D, PV>(s0, ka, x.rk, x.rv, x.goff);
+  lkeys<D, GATHER>(kb, x.ridx, 32, x.ebase);
   if (nsteps == 1) {
-    lstep<D, GATHER, PV, true, true, false>(st, x, q, s0, s1, kn, 0);
+    lstep<D, GATHER, PV, true, true, false>(st, x, q, s0, s1, kb, ka, 0);
     return;
   }
-  lstep<D, GATHER, PV, true, false, true>(st, x, q, s0, s1, kn, 0);
+  lstep<D, GATHER, PV, true, false, true>(st, x, q, s0, s1, kb, ka, 0);
   int it = 1;
   for (; it + 2 < nsteps; it += 2) {
-    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, kn, it);
-    lstep<D, GATHER, PV, false, false, true>(st, x, q, s0, s1, kn, it + 1);
+    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, ka, kb, it);
+    lstep<D, GATHER, PV, false, false, true>(st, x, q, s0, s1, kb, ka, it + 1);
   }
   // it is odd: stage s1 holds step it
   if (it + 1 < nsteps) {
-    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, kn, it);
-    lstep<D, GATHER, PV, false, true, false>(st, x, q, s0, s1, kn, it + 1);
+    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, ka, kb, it);
+    lstep<D, GATHER, PV, false, true, false>(st, x, q, s0, s1, kb, ka, it + 1);
   } else {
-    lstep<D, GATHER, PV, false, true, false>(st, x, q, s1, s0, kn, it);
+    lstep<D, GATHER, PV, false, true, false>(st, x, q, s1, s0, ka, kb, it);
   }
 }
 
