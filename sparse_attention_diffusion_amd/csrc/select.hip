@@ -45,16 +45,25 @@ struct WaveLds {
   int32_t cand_id[kCandCap];
 };
 
-__device__ __forceinline__ uint32_t lane_excl_scan(uint32_t x, uint32_t& total) {
-  const int lane = threadIdx.x & 63;
-  uint32_t v = x;
+// Ranks of this lane's flagged entries among the flagged entries of a 64 x 4
+// block ordered lane-major, then by j: rank[j] = flagged entries before (lane, j).
+// Returns the block's total.  Ballots and mbcnt, no cross-lane shuffles: the
+// shuffle-based scans these replace were latency bound (one wave per SIMD).
+__device__ __forceinline__ uint32_t flag_ranks(const bool (&f)[4], uint32_t (&rank)[4]) {
+  uint32_t before = 0, total = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)v, o, 64);
-    if (lane >= o) v += y;
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(f[j]);
+    before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, before));
+    total += (uint32_t)__builtin_popcountll(m);
   }
-  total = (uint32_t)__shfl((int)v, 63, 64);
-  return v - x;
+  uint32_t within = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rank[j] = before + within;
+    within += f[j] ? 1u : 0u;
+  }
+  return total;
 }
 
 // Digit (from the top) holding the kr-th largest entry of a wave-private histogram
@@ -110,6 +119,23 @@ __device__ __forceinline__ void load_batch(const uint32_t* rb, int N, int base, 
   }
 }
 
+// Visit a row in batches of kBatch entries, the loads of batch n+1 in flight
+// while batch n is processed (the scan is bound by load latency, not by the
+// per-entry work).  f(base, b) sees entries base + 256*u + 4*lane + j.
+template <typename F>
+__device__ __forceinline__ void scan_row(const uint32_t* rb, int N, F&& f) {
+  uint32_t ba[kUnroll][4], bb[kUnroll][4];
+  load_batch(rb, N, 0, ba);
+  int base = 0;
+  for (; base + kBatch < N; base += 2 * kBatch) {
+    load_batch(rb, N, base + kBatch, bb);
+    f(base, ba);
+    if (base + 2 * kBatch < N) load_batch(rb, N, base + 2 * kBatch, ba);
+    f(base + kBatch, bb);
+  }
+  if (base < N) f(base, ba);
+}
+
 // Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
 // id.  `w->hist` already holds the 12-bit histogram (bits 30..19) of the row.
 __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out, WaveLds* w) {
@@ -119,17 +145,25 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
   uint32_t prefix = pick_digit(w->hist, kHistBins, kr, cnt) << 19;
   uint32_t pmask = 0xfffu << 19;
   int shift = 19;
-  // Refine the prefix while too many entries share it (rare): bits 18..7, then 6..0.
+  // Refine the prefix while too many entries share it: bits 18..7, then 6..0.
+  // (Common when the masses near the threshold are dense: a 12-bit bin then holds
+  // thousands of entries.)  The row is read in the same batches as below.
   while (cnt > (uint32_t)kCandCap && shift > 0) {
     const int nshift = shift >= 12 ? shift - 12 : 0;
     const int bins = 1 << (shift - nshift);
     const int hb = bins < 64 ? 64 : bins;
     for (int j = lane; j < hb; j += 64) w->hist[j] = 0;
     __builtin_amdgcn_s_waitcnt(0);
-    for (int i = lane; i < N; i += 64) {
-      const uint32_t b = rb[i];
-      if ((b & pmask) == prefix) atomicAdd(&w->hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
-    }
+    scan_row(rb, N, [&](int base, const uint32_t (&b)[kUnroll][4]) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = base + 256 * u + 4 * lane + j;
+          if (i < N && (b[u][j] & pmask) == prefix)
+            atomicAdd(&w->hist[(b[u][j] >> nshift) & (uint32_t)(bins - 1)], 1u);
+        }
+    });
     __builtin_amdgcn_s_waitcnt(0);
     const uint32_t d = pick_digit(w->hist, hb, kr, cnt);
     prefix |= d << nshift;
@@ -139,30 +173,26 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
   // Candidates: entries matching the prefix, in ascending id order.  The row is
   // read in batches of 8 x 256 entries (8 independent 16-byte loads per lane).
   uint32_t nc = 0;
-  for (int base = 0; base < N; base += kBatch) {
-    uint32_t b[kUnroll][4];
-    load_batch(rb, N, base, b);
+  scan_row(rb, N, [&](int base, const uint32_t (&b)[kUnroll][4]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i0 = base + 256 * u + 4 * lane;
-      uint32_t nm = 0;
+      bool f[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) nm += (i0 + j < N && (b[u][j] & pmask) == prefix) ? 1u : 0u;
-      uint32_t tot;
-      uint32_t pos = nc + lane_excl_scan(nm, tot);
+      for (int j = 0; j < 4; ++j) f[j] = i0 + j < N && (b[u][j] & pmask) == prefix;
+      uint32_t rank[4];
+      const uint32_t tot = flag_ranks(f, rank);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (i0 + j < N && (b[u][j] & pmask) == prefix) {
-          if (pos < (uint32_t)kCandCap) {
-            w->cand_bits[pos] = b[u][j];
-            w->cand_id[pos] = i0 + j;
-          }
-          ++pos;
+        const uint32_t pos = nc + rank[j];
+        if (f[j] && pos < (uint32_t)kCandCap) {
+          w->cand_bits[pos] = b[u][j];
+          w->cand_id[pos] = i0 + j;
         }
       }
       nc += tot;
     }
-  }
+  });
   if (nc > (uint32_t)kCandCap) nc = kCandCap;  // the refinement above keeps nc within the cap
   __builtin_amdgcn_s_waitcnt(0);
   // Resolve the remaining low bits among the candidates, 8 at a time.
@@ -183,45 +213,37 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
   }
   const uint32_t tau = prefix;  // the K-th largest bit pattern; keep kr of its ties
   // Ascending compaction, same batching: 4 consecutive entries per lane.
+  // The kept ids go out through a buffer descriptor covering exactly K entries,
+  // one store instruction per (u, j) whatever is kept (the rest aim past the
+  // range and are dropped): with a fixed number of stores per batch the
+  // compiler's wait for the next batch's loads need not cover them.
+  const auto rout = make_rsrc(out, (uint32_t)K * 4u);
   uint32_t written = 0, eq_seen = 0;
-  for (int base = 0; base < N; base += kBatch) {
-    uint32_t bb[kUnroll][4];
-    load_batch(rb, N, base, bb);
+  scan_row(rb, N, [&](int base, const uint32_t (&bb)[kUnroll][4]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i0 = base + 256 * u + 4 * lane;
       const uint32_t* b = bb[u];
-      uint32_t ngt = 0, neq = 0;
+      // entries above tau are kept; of those equal to tau, the first kr in id order
+      bool eq[4], keep[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) eq[j] = i0 + j < N && b[j] == tau;
+      uint32_t eq_rank[4];
+      const uint32_t eq_tot = flag_ranks(eq, eq_rank);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) keep[j] = (i0 + j < N && b[j] > tau) || (eq[j] && eq_seen + eq_rank[j] < kr);
+      uint32_t rank[4];
+      const uint32_t sel_tot = flag_ranks(keep, rank);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool in = i0 + j < N;
-        ngt += (in && b[j] > tau) ? 1u : 0u;
-        neq += (in && b[j] == tau) ? 1u : 0u;
-      }
-      uint32_t eq_tot;
-      const uint32_t eq_before = eq_seen + lane_excl_scan(neq, eq_tot);
-      uint32_t take_eq = 0;
-      if (eq_before < kr) take_eq = min(neq, kr - eq_before);
-      uint32_t sel_tot;
-      uint32_t pos = written + lane_excl_scan(ngt + take_eq, sel_tot);
-      uint32_t left = take_eq;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool in = i0 + j < N;
-        bool keep = in && b[j] > tau;
-        if (in && b[j] == tau && left > 0) {
-          keep = true;
-          --left;
-        }
-        if (keep) {
-          if (pos < (uint32_t)K) out[pos] = i0 + j;  // exactly K are kept; stay in the row regardless
-          ++pos;
-        }
+        uint32_t off = keep[j] ? (written + rank[j]) * 4u : 0xfffffff0u;  // exactly K are kept overall
+        asm volatile("" : "+v"(off));  // opaque: keeps the store out of a branch on keep[j]
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(i0 + j), rout, off, 0, 0);
       }
       written += sel_tot;
       eq_seen += eq_tot;
     }
-  }
+  });
   for (int j = K + lane; j < kpad; j += 64) out[j] = -1;
 }
 
