@@ -10,17 +10,23 @@
 // in one launch per stage:
 //   1. stats   : per node, shifted sums  s = sum(x - r),  S = sum (x - r)(x - r)^T
 //                with r the node's first query (exact zero for identical queries,
-//                and no large-mean cancellation); S on v_mfma_f32_32x32x2_f32.
-//                Big nodes are split over several blocks that write partials.
+//                and no large-mean cancellation).  bf16 input: S on the bf16 MFMA
+//                from a two-plane split of x - r (exact products); fp32 input: S
+//                on v_mfma_f32_32x32x2_f32.  Big nodes are split over several
+//                blocks that write partials.
 //   2. power   : mean mu = r + s/n, covariance  C = S - n*m*m^T  (m = s/n), then a
 //                fixed number of power steps from ones/sqrt(D) (stop only if
-//                |C v| = 0); fused into stage 1 when one block holds the node.
+//                |C v| = 0); fused into stage 1 when one block holds the node
+//                (bf16: on the covariance as the MFMA left it, in registers).
 //   3. project : p = (x - mu) . v for every slot, as an order-preserving uint32.
 //   4. split   : per node, radix select of the rank-cut element of the 64-bit
 //                composite (projection key, token id), then a stable partition of
 //                the node's slots: smaller composites to the left child.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ldstile.hpp"
+
+#include <type_traits>
 
 namespace mcs {
 
@@ -328,6 +334,316 @@ __global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, 
   power_and_store<D>(cov, msh, ref, nd.n, a.iters, vbuf, red, w.node_param + ((size_t)h * maxn + k) * 2 * D);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 statistics on the bf16 MFMA.
+//
+// A node's shifted rows d = x - r (x, r bf16; d exact in fp32) are staged in LDS
+// as two bf16 planes, hi = bf16(d) and lo = bf16(d - hi).  hi + lo = d exactly
+// when |x| and |r| are within a factor 2^7 of each other, and to about 2^-17
+// relative otherwise.  Then
+//   S = sum d d^T = sum (hi hi^T + hi lo^T + lo hi^T + lo lo^T),
+// four v_mfma_f32_32x32x16_bf16 per 16 rows and 32x32 tile: every product is
+// exact in fp32 and the sums are fp32, as on the fp32 MFMA, at a quarter of its
+// issue cost.  Wave w owns accumulator tiles (ta, tb): ta = w, tb = 0..3 at
+// D = 128; (w / 2, w % 2) at D = 64.
+//
+// The MFMA operands of S = X^T X are columns of X (one dimension per lane, 8 rows
+// per lane in its k-slots), read from the row-major planes with the gfx950
+// transposing read ds_read_b64_tr_b16: within a 16-lane group, lane j receives
+// element j % 4 of the 8-byte pieces addressed by lanes 4t + j / 4, t = 0..3.
+// Lane m of group q addresses row 4*(q / 2) + m / 4 (+ 8 for the second read) and
+// dims 16*(q % 2) + 4*(m % 4) of the tile, so lane l ends up with dimension l % 32
+// of row 8*s + 4*(l / 32) + t in k-slot 4*s + t (s = read, t = 0..3).  A and B
+// use the same slot -> row map, and the 16 rows of a k-step each appear once.
+//
+// Plane rows are 2D bytes with the 32-byte units of row r XOR-ed by r % 4, so the
+// four rows one 16-lane group reads fall in four different 32-byte units.
+template <int D>
+struct BStats {
+  static constexpr int TR = 32;                // rows per tile: two 16-row k-steps
+  static constexpr int ROWB = 2 * D;           // bytes per plane row
+  static constexpr int PLANE = TR * ROWB;
+  static constexpr int BUF = 2 * PLANE;        // hi plane, then lo plane
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int RSTEP = kThreads / CH;  // rows between the chunks one thread stages
+  static constexpr int ITEMS = TR / RSTEP;     // chunks staged per thread per tile
+  static constexpr int NTA = D / 32;           // 32-dim tiles per side
+  static constexpr int TPW = NTA * NTA / 4;    // accumulator tiles per wave
+  // LDS carve-up (bytes).  The column-sum partials reuse the tile buffers after
+  // the last tile.
+  static constexpr int OFF_PART = 2 * BUF;                    // [2][NTA][D] power partials
+  static constexpr int OFF_VW = OFF_PART + 2 * NTA * D * 4;   // [4][D] direction, one copy per wave
+  static constexpr int OFF_VEC = OFF_VW + 4 * D * 4;          // ref[D], m[D]
+  static constexpr int BYTES = OFF_VEC + 2 * D * 4;
+  static_assert(RSTEP * D * 4 <= 2 * BUF, "column-sum partials fit the tile buffers");
+  static_assert(ITEMS * RSTEP == TR, "tile rows split evenly over the staging threads");
+  __device__ static int off(int row, int c) { return row * ROWB + (((c >> 1) ^ (row & 3)) << 5) + ((c & 1) << 4); }
+};
+
+// Lane byte offset (within a plane, first k-step) of the transposing reads of
+// 32-dim tile `tile`.
+template <int D>
+__device__ __forceinline__ int tr_lane_off(int lane, int tile) {
+  const int q = lane >> 4, m = lane & 15;
+  const int row = 4 * (q >> 1) + (m >> 2);  // row % 4 == m / 4
+  return row * BStats<D>::ROWB + (((2 * tile + (q & 1)) ^ (m >> 2)) << 5) + 8 * (m & 3);
+}
+
+// One MFMA operand: dimension lane % 32 of the lane's 8 rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_read(const LDSP char* p) {
+  typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+  const bf4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)p);
+  const bf4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(p + 8 * BStats<D>::ROWB));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row-major D x D store of accumulator tiles (a = 32*ta + row of the tile,
+// b = 32*tb + lane % 32).
+template <int D, int TPW>
+__device__ void store_acc(const f32x16 (&acc)[TPW], int ta, int tb0, float* dst) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, lm = lane & 31;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int b = 32 * (tb0 + t) + lm;
+      dst[a * D + b] = acc[t][r];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
+  using B = BStats<D>;
+  extern __shared__ float smem[];
+  const int P = lv.parts;
+  const int per_head = lv.nodes * P;
+  const int h = blockIdx.x / per_head;
+  const int rem = blockIdx.x - h * per_head;
+  const int k = rem / P, part = rem - k * P;
+  const Node nd = walk_node(a.N, a.C, lv.level, k);
+  if (!nd.internal) return;
+  const int chunk = (nd.n + P - 1) / P;
+  const int r0 = nd.start + part * chunk;
+  const int r1 = min(nd.start + nd.n, r0 + chunk);
+  const int ntiles = r1 > r0 ? (r1 - r0 + B::TR - 1) / B::TR : 0;
+  const bf16* qh = (const bf16*)a.q + (size_t)h * a.N * D;
+  const int32_t* permh = a.perm + (size_t)h * a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
+  LDSP char* lds = (LDSP char*)smem;
+
+  // Staging: thread tid converts chunk c of rows rbase + RSTEP*j of each tile.
+  const int c = tid % B::CH, rbase = tid / B::CH;
+  const int tok0 = permh[nd.start];
+  float refc[8];
+  chunk_to_f32<bf16>(*reinterpret_cast<const u32x4*>(qh + (size_t)tok0 * D + 8 * c), refc);
+  float cs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cs[i] = 0.0f;
+
+  auto load_toks = [&](int tile, int (&tk)[B::ITEMS]) {
+#pragma unroll
+    for (int j = 0; j < B::ITEMS; ++j) {
+      const int row = r0 + tile * B::TR + rbase + B::RSTEP * j;
+      tk[j] = row < r1 ? permh[row] : -1;
+    }
+  };
+  auto load_rows = [&](const int (&tk)[B::ITEMS], u32x4 (&xv)[B::ITEMS]) {
+#pragma unroll
+    for (int j = 0; j < B::ITEMS; ++j)
+      xv[j] = *reinterpret_cast<const u32x4*>(qh + (size_t)(tk[j] < 0 ? tok0 : tk[j]) * D + 8 * c);
+  };
+  auto stage = [&](LDSP char* buf, const int (&tk)[B::ITEMS], const u32x4 (&xv)[B::ITEMS]) {
+#pragma unroll
+    for (int j = 0; j < B::ITEMS; ++j) {
+      float x[8];
+      chunk_to_f32<bf16>(xv[j], x);
+      const bool ok = tk[j] >= 0;  // rows past the node contribute zero
+      u32x4 hw, lw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d0 = ok ? x[2 * i] - refc[2 * i] : 0.0f;
+        const float d1 = ok ? x[2 * i + 1] - refc[2 * i + 1] : 0.0f;
+        cs[2 * i] += d0;
+        cs[2 * i + 1] += d1;
+        hw[i] = pack_bf16x2(d0, d1);
+        lw[i] = pack_bf16x2(d0 - bf16lo(hw[i]), d1 - bf16hi(hw[i]));
+      }
+      const int off = B::off(rbase + B::RSTEP * j, c);
+      *(LDSP u32x4*)(buf + off) = hw;
+      *(LDSP u32x4*)(buf + B::PLANE + off) = lw;
+    }
+  };
+
+  const int ta = D == 128 ? wid : (wid >> 1);
+  const int tb0 = D == 128 ? 0 : (wid & 1);
+  const int aoff = tr_lane_off<D>(lane, ta);
+  int boff[B::TPW];
+#pragma unroll
+  for (int t = 0; t < B::TPW; ++t) boff[t] = tr_lane_off<D>(lane, tb0 + t);
+  f32x16 acc[B::TPW];
+#pragma unroll
+  for (int t = 0; t < B::TPW; ++t) acc[t] = f32x16{};
+
+  auto mma_tile = [&](const LDSP char* buf) {
+#pragma unroll
+    for (int ks = 0; ks < B::TR / 16; ++ks) {
+      const LDSP char* base = buf + 16 * ks * B::ROWB;
+      const bf16x8 ah = tr_read<D>(base + aoff), al = tr_read<D>(base + B::PLANE + aoff);
+      bf16x8 bh[B::TPW], bl[B::TPW];
+#pragma unroll
+      for (int t = 0; t < B::TPW; ++t) {
+        bh[t] = tr_read<D>(base + boff[t]);
+        bl[t] = tr_read<D>(base + B::PLANE + boff[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < B::TPW; ++t) acc[t] = mfma_bf16(ah, bh[t], acc[t]);
+#pragma unroll
+      for (int t = 0; t < B::TPW; ++t) acc[t] = mfma_bf16(ah, bl[t], acc[t]);
+#pragma unroll
+      for (int t = 0; t < B::TPW; ++t) acc[t] = mfma_bf16(al, bh[t], acc[t]);
+#pragma unroll
+      for (int t = 0; t < B::TPW; ++t) acc[t] = mfma_bf16(al, bl[t], acc[t]);
+    }
+  };
+
+  // Tile t is read from buffer t % 2 while tile t + 1 (loaded into registers
+  // before the MFMAs) is converted into the other one; one barrier per tile.
+  int tk[B::ITEMS], tkn[B::ITEMS];
+  u32x4 xv[B::ITEMS];
+  if (ntiles > 0) {
+    load_toks(0, tk);
+    load_rows(tk, xv);
+    if (ntiles > 1) load_toks(1, tkn);
+    stage(lds, tk, xv);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < B::ITEMS; ++j) tk[j] = tkn[j];
+      load_rows(tk, xv);
+      if (t + 2 < ntiles) load_toks(t + 2, tkn);
+    }
+    mma_tile(lds + (t & 1) * B::BUF);
+    if (more) stage(lds + ((t + 1) & 1) * B::BUF, tk, xv);
+    __syncthreads();
+  }
+
+  // Column sums: per-thread partials (tile buffers are free now), then one
+  // fixed-order sum per dimension.
+  float* csp = smem;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) csp[rbase * D + 8 * c + i] = cs[i];
+  __syncthreads();
+  float colsum = 0.0f;
+  if (tid < D)
+    for (int rr = 0; rr < B::RSTEP; ++rr) colsum += csp[rr * D + tid];
+
+  if (P > 1) {
+    float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)k * P + part) * (D + (size_t)D * D);
+    if (tid < D) dst[tid] = colsum;
+    store_acc<D, B::TPW>(acc, ta, tb0, dst + D);
+    return;
+  }
+
+  // Power iteration on C = S - n m m^T held in the accumulators.  Lane l holds
+  // C[a][b] for b = 32*(tb0 + t) + l % 32 and the 16 a = 32*ta + 8*(r/4) +
+  // 4*(l/32) + r%4; as C is symmetric, (C v)[b] = sum_a C[a][b] v[a], summed in
+  // the lane, then over the two lane halves, then over the a-tiles through LDS.
+  // Every wave forms the whole new vector (same data, same order: bitwise equal
+  // in every wave, so the zero-norm exit is uniform) and keeps its own copy.
+  float* partb = smem + B::OFF_PART / 4;
+  float* vwave = smem + B::OFF_VW / 4 + wid * D;
+  float* vec = smem + B::OFF_VEC / 4;  // ref[D], m[D]
+  if (tid < D) vec[D + tid] = colsum / (float)nd.n;
+  if (tid < B::CH)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vec[8 * c + i] = refc[i];
+  for (int e = lane; e < D; e += 64) vwave[e] = 1.0f / sqrtf((float)D);
+  __syncthreads();
+  {
+    float ma[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ma[r] = vec[D + 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3)];
+#pragma unroll
+    for (int t = 0; t < B::TPW; ++t) {
+      const float mb = vec[D + 32 * (tb0 + t) + lm];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] -= (float)nd.n * ma[r] * mb;
+    }
+  }
+  for (int it = 0; it < a.iters; ++it) {
+    float va[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v4 = *(const f32x4*)(vwave + 32 * ta + 8 * j + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va[4 * j + i] = v4[i];
+    }
+    float* pw = partb + (it & 1) * B::NTA * D;
+#pragma unroll
+    for (int t = 0; t < B::TPW; ++t) {
+      float p = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p = __builtin_fmaf(acc[t][r], va[r], p);
+      p = pair_sum(p);
+      if (hf == 0) pw[ta * D + 32 * (tb0 + t) + lm] = p;
+    }
+    __syncthreads();  // the buffer written here is rewritten two steps later, after the next barrier
+    constexpr int PER = D / 64;
+    float wv[PER];
+    float sq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      float s = 0.0f;
+#pragma unroll
+      for (int t2 = 0; t2 < B::NTA; ++t2) s += pw[t2 * D + lane + 64 * j];
+      wv[j] = s;
+      sq = __builtin_fmaf(s, s, sq);
+    }
+    sq = wave_sum_dpp(sq);
+    if (sq == 0.0f) break;
+    const float inv = 1.0f / sqrtf(sq);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vwave[lane + 64 * j] = wv[j] * inv;
+  }
+  if (wid == 0) {
+    const int maxn = 1 << lv.level;
+    float* out = w.node_param + ((size_t)h * maxn + k) * 2 * D;
+    for (int e = lane; e < D; e += 64) {
+      out[e] = vec[e] + vec[D + e];  // mu
+      out[D + e] = vwave[e];         // v
+    }
+  }
+}
+
+// n consecutive elements (n * sizeof(T) a multiple of 8 bytes, naturally aligned)
+// as floats, with 16- or 8-byte loads.
+template <typename T, int n>
+__device__ __forceinline__ void load_dims(const T* p, float* out) {
+  if constexpr (sizeof(T) * n % 16 == 0) {
+#pragma unroll
+    for (int c = 0; c < (int)(sizeof(T) * n / 16); ++c)
+      chunk_to_f32<T>(reinterpret_cast<const u32x4*>(p)[c], out + c * (16 / (int)sizeof(T)));
+  } else {
+    static_assert(sizeof(T) * n == 8, "8-byte piece");
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    if constexpr (sizeof(T) == 2) {
+      out[0] = bf16lo(w[0]);
+      out[1] = bf16hi(w[0]);
+      out[2] = bf16lo(w[1]);
+      out[3] = bf16hi(w[1]);
+    } else {
+      out[0] = __uint_as_float(w[0]);
+      out[1] = __uint_as_float(w[1]);
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void pddp_project_kernel(PddpArgs a, Ws w, Level lv) {
   const int P = lv.parts;
@@ -345,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void pddp_project_kernel(PddpArgs a, Ws w
   const T* qh = (const T*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
   uint32_t* keys = w.keys + (size_t)h * a.N;
-  // 16 lanes per row, D/16 dims per lane.
+  // 16 lanes per row, D/16 consecutive dims per lane (one or two vector loads).
   constexpr int DPL = D / 16;
   const int tid = threadIdx.x, sub = tid & 15, rgrp = tid >> 4;
   float mu[DPL], v[DPL];
@@ -356,10 +672,11 @@ __global__ __launch_bounds__(kThreads) void pddp_project_kernel(PddpArgs a, Ws w
   }
   for (int row = r0 + rgrp; row < r1; row += kThreads / 16) {
     const int tok = permh[row];
-    const T* x = qh + (size_t)tok * D + sub * DPL;
+    float x[DPL];
+    load_dims<T, DPL>(qh + (size_t)tok * D + sub * DPL, x);
     float p = 0.0f;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(ldf(x + j) - mu[j], v[j], p);
+    for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(x[j] - mu[j], v[j], p);
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
     if (sub == 0) keys[row] = float_key(p);
@@ -536,25 +853,28 @@ hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int L = level_count(a.N, a.C);
   const size_t lds = (size_t)(stats_region_floats<T, D>() + 3 * D + 8 + kThreads) * sizeof(float);
-  // The statistics and power kernels hold a D x D covariance in LDS (64 KiB at
-  // D = 128), above the default dynamic-LDS limit.
-  if ((e = hipFuncSetAttribute((const void*)pddp_stats_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds)) != hipSuccess)
-    return e;
+  // The fp32 statistics and the power kernels hold a D x D covariance in LDS
+  // (64 KiB at D = 128), above the default dynamic-LDS limit.
+  if constexpr (!std::is_same<T, __bf16>::value) {
+    if ((e = hipFuncSetAttribute((const void*)pddp_stats_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds)) != hipSuccess)
+      return e;
+  }
   if ((e = hipFuncSetAttribute((const void*)pddp_power_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds)) != hipSuccess)
     return e;
   for (int l = 0; l < L; ++l) {
     Level lv{l, 1 << l, parts_for(a.N, l)};
     const unsigned nb = (unsigned)(a.H * lv.nodes * lv.parts);
-    if (lv.parts > 1) {
+    if constexpr (std::is_same<T, __bf16>::value)
+      hipLaunchKernelGGL((pddp_stats_bf16_kernel<D>), dim3(nb), dim3(kThreads), BStats<D>::BYTES, s, a, w, lv);
+    else
       hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), lds, s, a, w, lv);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), lds, s, a, w, lv);
-    } else {
-      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), lds, s, a, w, lv);
-    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (lv.parts > 1) {
+      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), lds, s, a, w, lv);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((pddp_project_kernel<T, D>), dim3(nb), dim3(kThreads), 0, s, a, w, lv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(w.tmp_perm, a.perm, total * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess) return e;

@@ -22,7 +22,9 @@ def _group_sizes_ok(perm, n):
 
 
 @pytest.mark.parametrize("grid,heads,d,dtype", [((8, 8, 16), 1, 64, "f32"), ((5, 9, 13), 3, 128, "bf16"),
-                                                  ((3, 7, 11), 2, 64, "bf16"), ((4, 16, 20), 2, 128, "f32")])
+                                                  ((3, 7, 11), 2, 64, "bf16"), ((4, 16, 20), 2, 128, "f32"),
+                                                  # several statistics blocks per node at the top levels
+                                                  ((16, 16, 33), 1, 128, "bf16"), ((12, 16, 25), 1, 64, "bf16")])
 def test_pddp_passes_node_local_verifier(grid, heads, d, dtype):
     q, _, _ = _grid_qk(grid, heads, d, dtype, seed=1)
     n = q.shape[1]
