@@ -122,12 +122,27 @@ struct StatsAcc {
   f32x16 acc[TPW];
 };
 
-// Shared-memory footprint of the statistics kernels (floats): the row tile and the
-// covariance never live at the same time, so they share one region.
+// Accumulator tiles of wave `wid`: a-tile ta, b-tiles tb0 .. tb0 + TPW - 1.
+template <int D>
+__device__ __forceinline__ int acc_ta(int wid) { return D == 128 ? wid : (wid >> 1); }
+template <int D>
+__device__ __forceinline__ int acc_tb0(int wid) { return D == 128 ? 0 : (wid & 1); }
+
+// LDS of the power iteration (floats): partial products [2][D/32][D], one copy of
+// the direction per wave [4][D], then ref[D] (the node's first query) and m[D]
+// (mean of x - ref).
+template <int D>
+struct PowLds {
+  static constexpr int PART = 0;
+  static constexpr int VW = PART + 2 * (D / 32) * D;
+  static constexpr int VEC = VW + 4 * D;
+  static constexpr int FLOATS = VEC + 2 * D;
+};
+
+// Floats of LDS of the fp32 statistics kernel: the row tile, then the power region.
 template <typename T, int D>
-constexpr int stats_region_floats() {
-  using SA = StatsAcc<T, D>;
-  return SA::TILE_ROWS * SA::LDX > D * D ? SA::TILE_ROWS * SA::LDX : D * D;
+constexpr int stats_f32_lds_floats() {
+  return StatsAcc<T, D>::TILE_ROWS * StatsAcc<T, D>::LDX + PowLds<D>::FLOATS;
 }
 
 template <typename T>
@@ -144,6 +159,49 @@ template <>
 __device__ __forceinline__ void chunk_to_f32<float>(u32x4 w, float* out) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+}
+
+// n consecutive elements (n * sizeof(T) a multiple of 8 bytes, naturally aligned)
+// as floats, with 16- or 8-byte loads.
+template <typename T, int n>
+__device__ __forceinline__ void load_dims(const T* p, float* out) {
+  if constexpr (sizeof(T) * n % 16 == 0) {
+#pragma unroll
+    for (int c = 0; c < (int)(sizeof(T) * n / 16); ++c)
+      chunk_to_f32<T>(reinterpret_cast<const u32x4*>(p)[c], out + c * (16 / (int)sizeof(T)));
+  } else {
+    static_assert(sizeof(T) * n == 8, "8-byte piece");
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    if constexpr (sizeof(T) == 2) {
+      out[0] = bf16lo(w[0]);
+      out[1] = bf16hi(w[0]);
+      out[2] = bf16lo(w[1]);
+      out[3] = bf16hi(w[1]);
+    } else {
+      out[0] = __uint_as_float(w[0]);
+      out[1] = __uint_as_float(w[1]);
+    }
+  }
+}
+
+// Projection keys of slots [r0, r1): key = float_key((x - mu) . v), 16 lanes per
+// row, D/16 consecutive dims per lane (lane `sub` holds mu and v of its dims).
+template <typename T, int D>
+__device__ __forceinline__ void project_rows(const T* qh, const int32_t* permh, uint32_t* keys, int r0, int r1,
+                                             const float (&mu)[D / 16], const float (&v)[D / 16]) {
+  constexpr int DPL = D / 16;
+  const int tid = threadIdx.x, sub = tid & 15, rgrp = tid >> 4;
+  for (int row = r0 + rgrp; row < r1; row += kThreads / 16) {
+    const int tok = permh[row];
+    float x[DPL];
+    load_dims<T, DPL>(qh + (size_t)tok * D + sub * DPL, x);
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(x[j] - mu[j], v[j], p);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
+    if (sub == 0) keys[row] = float_key(p);
+  }
 }
 
 // Accumulate the shifted sums of rows [r0, r1) of a node (slots, mapped through
@@ -194,67 +252,111 @@ __device__ void stats_rows(const T* qh, const int32_t* permh, const float* ref, 
   }
 }
 
-// Write the accumulated S tiles into a row-major D x D destination (LDS or global).
-template <typename T, int D>
-__device__ void store_tiles(const StatsAcc<T, D>& sa, float* dst) {
-  const int lane = threadIdx.x & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
+// Row-major D x D store of accumulator tiles (a = 32*ta + row of the tile,
+// b = 32*tb + lane % 32).
+template <int D, int TPW>
+__device__ void store_acc(const f32x16 (&acc)[TPW], int ta, int tb0, float* dst) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, lm = lane & 31;
 #pragma unroll
-  for (int t = 0; t < StatsAcc<T, D>::TPW; ++t) {
-    const int ta = D == 128 ? wid : (wid >> 1);
-    const int tb = D == 128 ? t : (wid & 1);
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int a = 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const int b = 32 * tb + lm;
-      dst[a * D + b] = sa.acc[t][r];
+      const int b = 32 * (tb0 + t) + lm;
+      dst[a * D + b] = acc[t][r];
+    }
+}
+
+// Power iteration on C = S - n m m^T, with S in MFMA accumulator tiles: lane l of
+// a wave holds S[a][b] for b = 32*(tb0 + t) + l % 32 and the 16 a = 32*ta +
+// 8*(r/4) + 4*(l/32) + r%4 (r = accumulator register).  pl is the PowLds region,
+// with ref and m filled in and visible to the whole block.
+//
+// C is symmetric, so (C v)[b] = sum_a C[a][b] v[a]: summed within the lane, then
+// over the two lane halves, then over the a-tiles through LDS (one barrier per
+// step; the partial buffers alternate, and a buffer is rewritten only after the
+// next barrier).  Every wave forms the whole new vector from the same data in the
+// same order, so all waves hold bitwise equal copies and take the zero-norm exit
+// together; each keeps its own copy, which is left in pl + VW + wave*D.  Wave 0
+// writes {mu = ref + m, v} to out.
+template <int D, int TPW>
+__device__ __forceinline__ void power_regs(f32x16 (&acc)[TPW], int ta, int tb0, int n, int iters, float* pl,
+                                           float* out) {
+  constexpr int NTA = D / 32;
+  const int lane = threadIdx.x & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
+  float* partb = pl + PowLds<D>::PART;
+  float* vwave = pl + PowLds<D>::VW + wid * D;
+  const float* vec = pl + PowLds<D>::VEC;
+  {
+    float ma[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ma[r] = vec[D + 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3)];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float mb = vec[D + 32 * (tb0 + t) + lm];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] -= (float)n * ma[r] * mb;
+    }
+  }
+  for (int e = lane; e < D; e += 64) vwave[e] = 1.0f / sqrtf((float)D);
+  for (int it = 0; it < iters; ++it) {
+    float va[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v4 = *(const f32x4*)(vwave + 32 * ta + 8 * j + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va[4 * j + i] = v4[i];
+    }
+    float* pw = partb + (it & 1) * NTA * D;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float p = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p = __builtin_fmaf(acc[t][r], va[r], p);
+      p = pair_sum(p);
+      if (hf == 0) pw[ta * D + 32 * (tb0 + t) + lm] = p;
+    }
+    __syncthreads();
+    constexpr int PER = D / 64;
+    float wv[PER];
+    float sq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      float s = 0.0f;
+#pragma unroll
+      for (int t2 = 0; t2 < NTA; ++t2) s += pw[t2 * D + lane + 64 * j];
+      wv[j] = s;
+      sq = __builtin_fmaf(s, s, sq);
+    }
+    sq = wave_sum_dpp(sq);
+    if (sq == 0.0f) break;
+    const float inv = 1.0f / sqrtf(sq);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vwave[lane + 64 * j] = wv[j] * inv;
+  }
+  if (wid == 0) {
+    for (int e = lane; e < D; e += 64) {
+      out[e] = vec[e] + vec[D + e];  // mu
+      out[D + e] = vwave[e];         // v
     }
   }
 }
 
-// Power iteration on the centred covariance held in LDS; writes mu and v.
-// The covariance is symmetric, so w[a] = sum_b C[b][a] v[b] reads C by columns:
-// consecutive lanes touch consecutive addresses (no bank conflicts).
-template <int D>
-__device__ void power_and_store(float* cov, const float* m_shift, const float* ref, int n, int iters, float* vbuf,
-                                float* red, float* out_param) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < D * D; e += kThreads) {
-    const int a = e / D, b = e - a * D;
-    cov[e] -= (float)n * m_shift[a] * m_shift[b];
+// After power_regs: projections of the node's slots with this wave's copy of v.
+template <typename T, int D>
+__device__ __forceinline__ void project_node(const T* qh, const int32_t* permh, uint32_t* keys, int r0, int r1,
+                                             const float* pl) {
+  constexpr int DPL = D / 16;
+  const int sub = threadIdx.x & 15;
+  const float* vwave = pl + PowLds<D>::VW + wave_id() * D;
+  const float* vec = pl + PowLds<D>::VEC;
+  float mu[DPL], v[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
+    mu[j] = vec[sub * DPL + j] + vec[D + sub * DPL + j];
+    v[j] = vwave[sub * DPL + j];
   }
-  if (tid < D) vbuf[tid] = 1.0f / sqrtf((float)D);
-  __syncthreads();
-  constexpr int PARTS = kThreads / D;  // column partitions (2 at D = 128, 4 at D = 64)
-  constexpr int BPP = D / PARTS;
-  const int a = tid % D, part = tid / D;
-  float* wpart = red + 8;              // PARTS * D partial sums
-  for (int it = 0; it < iters; ++it) {
-    float w = 0.0f;
-#pragma unroll 8
-    for (int j = 0; j < BPP; ++j) {
-      const int b = part * BPP + j;
-      w = __builtin_fmaf(cov[b * D + a], vbuf[b], w);
-    }
-    wpart[part * D + a] = w;
-    __syncthreads();
-    float wa = 0.0f, sq = 0.0f;
-    if (tid < D) {
-      for (int p = 0; p < PARTS; ++p) wa += wpart[p * D + tid];
-      sq = wa * wa;
-    }
-    sq = wave_sum(sq);
-    if ((tid & 63) == 0) red[tid >> 6] = sq;
-    __syncthreads();
-    const float nrm2 = red[0] + red[1] + red[2] + red[3];
-    if (nrm2 == 0.0f) break;  // uniform: every thread read the same sum
-    if (tid < D) vbuf[tid] = wa * (1.0f / sqrtf(nrm2));
-    __syncthreads();
-  }
-  __syncthreads();
-  if (tid < D) {
-    out_param[tid] = ref[tid] + m_shift[tid];  // mu
-    out_param[D + tid] = vbuf[tid];            // v
-  }
+  project_rows<T, D>(qh, permh, keys, r0, r1, mu, v);
 }
 
 template <typename T, int D>
@@ -274,36 +376,36 @@ __global__ __launch_bounds__(kThreads) void pddp_stats_kernel(PddpArgs a, Ws w, 
   const T* qh = (const T*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
 
-  float* region = smem;                                 // row tile, later the covariance
-  float* ref = region + stats_region_floats<T, D>();    // D
-  float* msh = ref + D;                                 // D
-  float* vbuf = msh + D;                                // D
-  float* red = vbuf + D;                                // 8 + (threads / D) * D
-  const int tid = threadIdx.x;
+  float* tile = smem;                                       // row tile
+  float* pl = smem + SA::TILE_ROWS * SA::LDX;               // power region
+  float* vec = pl + PowLds<D>::VEC;                         // ref[D], m[D]
+  const int tid = threadIdx.x, wid = wave_id();
   const int tok0 = permh[nd.start];
-  if (tid < D) ref[tid] = ldf(qh + (size_t)tok0 * D + tid);
+  if (tid < D) vec[tid] = ldf(qh + (size_t)tok0 * D + tid);
   __syncthreads();
   SA sa;
   float colsum;
-  stats_rows<T, D>(qh, permh, ref, r0, max(r1, r0), region, sa, colsum);
+  stats_rows<T, D>(qh, permh, vec, r0, max(r1, r0), tile, sa, colsum);
   if (P > 1) {
     float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)k * P + part) * (D + (size_t)D * D);
     if (tid < D) dst[tid] = colsum;
-    store_tiles<T, D>(sa, dst + D);
+    store_acc<D, SA::TPW>(sa.acc, acc_ta<D>(wid), acc_tb0<D>(wid), dst + D);
     return;
   }
-  __syncthreads();  // all MFMA reads of the row tile are done before it becomes the covariance
-  store_tiles<T, D>(sa, region);
-  if (tid < D) msh[tid] = colsum / (float)nd.n;
+  if (tid < D) vec[D + tid] = colsum / (float)nd.n;
   __syncthreads();
   const int maxn = 1 << lv.level;
-  power_and_store<D>(region, msh, ref, nd.n, a.iters, vbuf, red,
-                     w.node_param + ((size_t)h * maxn + k) * 2 * D);
+  power_regs<D, SA::TPW>(sa.acc, acc_ta<D>(wid), acc_tb0<D>(wid), nd.n, a.iters, pl,
+                         w.node_param + ((size_t)h * maxn + k) * 2 * D);
+  project_node<T, D>(qh, permh, w.keys + (size_t)h * a.N, nd.start, nd.start + nd.n, pl);
 }
 
+// Nodes split over several statistics blocks: fixed-order sums of their partials
+// (column sums, then S straight into the accumulator layout), then power_regs.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, Level lv) {
-  extern __shared__ float smem[];
+  extern __shared__ float smem[];  // PowLds<D>
+  constexpr int TPW = (D / 32) * (D / 32) / 4;
   const int h = blockIdx.x / lv.nodes;
   const int k = blockIdx.x - h * lv.nodes;
   const Node nd = walk_node(a.N, a.C, lv.level, k);
@@ -311,27 +413,31 @@ __global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, 
   const int P = lv.parts;
   const T* qh = (const T*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
-  float* cov = smem;                               // D*D
-  float* ref = cov + stats_region_floats<T, D>();  // D
-  float* msh = ref + D;                            // D
-  float* vbuf = msh + D;                           // D
-  float* red = vbuf + D;                           // 8 + (threads / D) * D
-  const int tid = threadIdx.x;
-  const float* src = w.partials + ((size_t)h * kMaxParts + (size_t)k * P) * (D + (size_t)D * D);
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
   const size_t stride = D + (size_t)D * D;
-  for (int e = tid; e < D + D * D; e += kThreads) {
+  const float* src = w.partials + ((size_t)h * kMaxParts + (size_t)k * P) * stride;
+  float* vec = smem + PowLds<D>::VEC;
+  if (tid < D) {
     float s = 0.0f;
 #pragma unroll 8
-    for (int p = 0; p < P; ++p) s += src[p * stride + e];  // fixed order: deterministic
-    if (e < D)
-      msh[e] = s / (float)nd.n;
-    else
-      cov[e - D] = s;
+    for (int p = 0; p < P; ++p) s += src[p * stride + tid];
+    vec[D + tid] = s / (float)nd.n;
+    vec[tid] = ldf(qh + (size_t)permh[nd.start] * D + tid);
   }
-  if (tid < D) ref[tid] = ldf(qh + (size_t)permh[nd.start] * D + tid);
+  const int ta = acc_ta<D>(wid), tb0 = acc_tb0<D>(wid);
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x16{};
+  for (int p = 0; p < P; ++p) {
+    const float* sp = src + p * stride + D;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] += sp[(32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3)) * D + 32 * (tb0 + t) + lm];
+  }
   __syncthreads();
   const int maxn = 1 << lv.level;
-  power_and_store<D>(cov, msh, ref, nd.n, a.iters, vbuf, red, w.node_param + ((size_t)h * maxn + k) * 2 * D);
+  power_regs<D, TPW>(acc, ta, tb0, nd.n, a.iters, smem, w.node_param + ((size_t)h * maxn + k) * 2 * D);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,12 +475,10 @@ struct BStats {
   static constexpr int ITEMS = TR / RSTEP;     // chunks staged per thread per tile
   static constexpr int NTA = D / 32;           // 32-dim tiles per side
   static constexpr int TPW = NTA * NTA / 4;    // accumulator tiles per wave
-  // LDS carve-up (bytes).  The column-sum partials reuse the tile buffers after
-  // the last tile.
-  static constexpr int OFF_PART = 2 * BUF;                    // [2][NTA][D] power partials
-  static constexpr int OFF_VW = OFF_PART + 2 * NTA * D * 4;   // [4][D] direction, one copy per wave
-  static constexpr int OFF_VEC = OFF_VW + 4 * D * 4;          // ref[D], m[D]
-  static constexpr int BYTES = OFF_VEC + 2 * D * 4;
+  // LDS carve-up (bytes): two tile buffers, then the power region.  The
+  // column-sum partials reuse the tile buffers after the last tile.
+  static constexpr int OFF_POW = 2 * BUF;
+  static constexpr int BYTES = OFF_POW + PowLds<D>::FLOATS * 4;
   static_assert(RSTEP * D * 4 <= 2 * BUF, "column-sum partials fit the tile buffers");
   static_assert(ITEMS * RSTEP == TR, "tile rows split evenly over the staging threads");
   __device__ static int off(int row, int c) { return row * ROWB + (((c >> 1) ^ (row & 3)) << 5) + ((c & 1) << 4); }
@@ -396,21 +500,6 @@ __device__ __forceinline__ bf16x8 tr_read(const LDSP char* p) {
   const bf4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)p);
   const bf4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(p + 8 * BStats<D>::ROWB));
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Row-major D x D store of accumulator tiles (a = 32*ta + row of the tile,
-// b = 32*tb + lane % 32).
-template <int D, int TPW>
-__device__ void store_acc(const f32x16 (&acc)[TPW], int ta, int tb0, float* dst) {
-  const int lane = threadIdx.x & 63, hf = lane >> 5, lm = lane & 31;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int a = 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const int b = 32 * (tb0 + t) + lm;
-      dst[a * D + b] = acc[t][r];
-    }
 }
 
 template <int D>
@@ -550,98 +639,16 @@ void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
     return;
   }
 
-  // Power iteration on C = S - n m m^T held in the accumulators.  Lane l holds
-  // C[a][b] for b = 32*(tb0 + t) + l % 32 and the 16 a = 32*ta + 8*(r/4) +
-  // 4*(l/32) + r%4; as C is symmetric, (C v)[b] = sum_a C[a][b] v[a], summed in
-  // the lane, then over the two lane halves, then over the a-tiles through LDS.
-  // Every wave forms the whole new vector (same data, same order: bitwise equal
-  // in every wave, so the zero-norm exit is uniform) and keeps its own copy.
-  float* partb = smem + B::OFF_PART / 4;
-  float* vwave = smem + B::OFF_VW / 4 + wid * D;
-  float* vec = smem + B::OFF_VEC / 4;  // ref[D], m[D]
+  const int maxn = 1 << lv.level;
+  float* pl = smem + B::OFF_POW / 4;
+  float* vec = pl + PowLds<D>::VEC;
   if (tid < D) vec[D + tid] = colsum / (float)nd.n;
   if (tid < B::CH)
 #pragma unroll
     for (int i = 0; i < 8; ++i) vec[8 * c + i] = refc[i];
-  for (int e = lane; e < D; e += 64) vwave[e] = 1.0f / sqrtf((float)D);
   __syncthreads();
-  {
-    float ma[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ma[r] = vec[D + 32 * ta + 8 * (r >> 2) + 4 * hf + (r & 3)];
-#pragma unroll
-    for (int t = 0; t < B::TPW; ++t) {
-      const float mb = vec[D + 32 * (tb0 + t) + lm];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] -= (float)nd.n * ma[r] * mb;
-    }
-  }
-  for (int it = 0; it < a.iters; ++it) {
-    float va[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 v4 = *(const f32x4*)(vwave + 32 * ta + 8 * j + 4 * hf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) va[4 * j + i] = v4[i];
-    }
-    float* pw = partb + (it & 1) * B::NTA * D;
-#pragma unroll
-    for (int t = 0; t < B::TPW; ++t) {
-      float p = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p = __builtin_fmaf(acc[t][r], va[r], p);
-      p = pair_sum(p);
-      if (hf == 0) pw[ta * D + 32 * (tb0 + t) + lm] = p;
-    }
-    __syncthreads();  // the buffer written here is rewritten two steps later, after the next barrier
-    constexpr int PER = D / 64;
-    float wv[PER];
-    float sq = 0.0f;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      float s = 0.0f;
-#pragma unroll
-      for (int t2 = 0; t2 < B::NTA; ++t2) s += pw[t2 * D + lane + 64 * j];
-      wv[j] = s;
-      sq = __builtin_fmaf(s, s, sq);
-    }
-    sq = wave_sum_dpp(sq);
-    if (sq == 0.0f) break;
-    const float inv = 1.0f / sqrtf(sq);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) vwave[lane + 64 * j] = wv[j] * inv;
-  }
-  if (wid == 0) {
-    const int maxn = 1 << lv.level;
-    float* out = w.node_param + ((size_t)h * maxn + k) * 2 * D;
-    for (int e = lane; e < D; e += 64) {
-      out[e] = vec[e] + vec[D + e];  // mu
-      out[D + e] = vwave[e];         // v
-    }
-  }
-}
-
-// n consecutive elements (n * sizeof(T) a multiple of 8 bytes, naturally aligned)
-// as floats, with 16- or 8-byte loads.
-template <typename T, int n>
-__device__ __forceinline__ void load_dims(const T* p, float* out) {
-  if constexpr (sizeof(T) * n % 16 == 0) {
-#pragma unroll
-    for (int c = 0; c < (int)(sizeof(T) * n / 16); ++c)
-      chunk_to_f32<T>(reinterpret_cast<const u32x4*>(p)[c], out + c * (16 / (int)sizeof(T)));
-  } else {
-    static_assert(sizeof(T) * n == 8, "8-byte piece");
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-    if constexpr (sizeof(T) == 2) {
-      out[0] = bf16lo(w[0]);
-      out[1] = bf16hi(w[0]);
-      out[2] = bf16lo(w[1]);
-      out[3] = bf16hi(w[1]);
-    } else {
-      out[0] = __uint_as_float(w[0]);
-      out[1] = __uint_as_float(w[1]);
-    }
-  }
+  power_regs<D, B::TPW>(acc, ta, tb0, nd.n, a.iters, pl, w.node_param + ((size_t)h * maxn + k) * 2 * D);
+  project_node<bf16, D>(qh, permh, w.keys + (size_t)h * a.N, nd.start, nd.start + nd.n, pl);
 }
 
 template <typename T, int D>
@@ -660,40 +667,36 @@ __global__ __launch_bounds__(kThreads) void pddp_project_kernel(PddpArgs a, Ws w
   const float* prm = w.node_param + ((size_t)h * maxn + k) * 2 * D;
   const T* qh = (const T*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
-  uint32_t* keys = w.keys + (size_t)h * a.N;
-  // 16 lanes per row, D/16 consecutive dims per lane (one or two vector loads).
+  // 16 lanes per row, D/16 consecutive dims per lane.
   constexpr int DPL = D / 16;
-  const int tid = threadIdx.x, sub = tid & 15, rgrp = tid >> 4;
+  const int sub = threadIdx.x & 15;
   float mu[DPL], v[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) {
     mu[j] = prm[sub * DPL + j];
     v[j] = prm[D + sub * DPL + j];
   }
-  for (int row = r0 + rgrp; row < r1; row += kThreads / 16) {
-    const int tok = permh[row];
-    float x[DPL];
-    load_dims<T, DPL>(qh + (size_t)tok * D + sub * DPL, x);
-    float p = 0.0f;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(x[j] - mu[j], v[j], p);
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
-    if (sub == 0) keys[row] = float_key(p);
-  }
+  project_rows<T, D>(qh, permh, w.keys + (size_t)h * a.N, r0, r1, mu, v);
 }
 
+// Histogram add of digit d for the active lanes: one LDS atomic for the wave when
+// every active lane has the same digit (the usual case for the high digits of a
+// node's keys), else one per lane.
 __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t d) {
-  uint64_t todo = __builtin_amdgcn_ballot_w64(active);
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
-    const uint64_t same = __builtin_amdgcn_ballot_w64(active && d == ld);
-    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[ld], (uint32_t)__builtin_popcountll(same));
-    todo &= ~same;
+  const uint64_t act = __builtin_amdgcn_ballot_w64(active);
+  if (act == 0) return;
+  const int leader = __builtin_ctzll(act);
+  const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+  const uint64_t same = __builtin_amdgcn_ballot_w64(active && d == ld);
+  if (same == act) {
+    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[ld], (uint32_t)__builtin_popcountll(act));
+  } else if (active) {
+    atomicAdd(&hist[d], 1u);
   }
 }
 
+// Inclusive block scan of x over NT threads; returns the block total.
+template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& incl) {
   const int lane = threadIdx.x & 63, wid = wave_id();
   uint32_t v = x;
@@ -706,7 +709,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint3
   __syncthreads();
   uint32_t before = 0, total = 0;
 #pragma unroll
-  for (int ww = 0; ww < kThreads / 64; ++ww) {
+  for (int ww = 0; ww < NT / 64; ++ww) {
     const uint32_t t = wsum[ww];
     if (ww < wid) before += t;
     total += t;
@@ -718,14 +721,17 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint3
 
 // One radix pass over the node: histogram of digit `shift` of the selected word
 // among entries whose already-fixed bits match; returns the digit holding rank kr
-// (0-based, ascending) and updates kr to the rank inside that digit.
+// (0-based, ascending) and updates kr to the rank inside that digit.  The digit is
+// the bin whose inclusive prefix count first exceeds kr, found by a block scan of
+// the 256 bins.
+template <int NT>
 __device__ uint32_t radix_pass(const uint32_t* keys, const int32_t* toks, int start, int n, bool use_tok,
                                uint32_t hi_val, uint32_t prefix, uint32_t pmask, int shift, uint32_t& kr,
-                               uint32_t* hist, uint32_t* bcast) {
+                               uint32_t* hist, uint32_t* wsum, uint32_t* bcast) {
   const int tid = threadIdx.x;
-  hist[tid] = 0;
+  for (int i = tid; i < 256; i += NT) hist[i] = 0;
   __syncthreads();
-  for (int b = 0; b < n; b += kThreads) {
+  for (int b = 0; b < n; b += NT) {
     const int i = b + tid;
     bool act = i < n;
     uint32_t word = 0;
@@ -742,26 +748,23 @@ __device__ uint32_t radix_pass(const uint32_t* keys, const int32_t* toks, int st
     hist_add(hist, act, (word >> shift) & 255u);
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t below = 0;
-    int d = 0;
-    for (; d < 255; ++d) {
-      if (below + hist[d] > kr) break;
-      below += hist[d];
-    }
-    bcast[0] = (uint32_t)d;
-    bcast[1] = kr - below;
+  const uint32_t cnt = tid < 256 ? hist[tid] : 0u;
+  uint32_t incl;
+  block_scan<NT>(cnt, wsum, incl);  // its barriers also order the hist reads before the next clear
+  if (tid < 256 && incl > kr && incl - cnt <= kr) {  // exactly one bin, as kr < the pass's count
+    bcast[0] = (uint32_t)tid;
+    bcast[1] = kr - (incl - cnt);
   }
   __syncthreads();
   const uint32_t d = bcast[0];
   kr = bcast[1];
-  __syncthreads();
-  return d;
+  return d;  // bcast is rewritten only after the next pass's barriers
 }
 
-__global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, Level lv) {
+template <int NT>
+__global__ __launch_bounds__(NT) void pddp_split_kernel(PddpArgs a, Ws w, Level lv) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[kThreads / 64];
+  __shared__ uint32_t wsum[NT / 64];
   __shared__ uint32_t bcast[2];
   const int h = blockIdx.x / lv.nodes;
   const int k = blockIdx.x - h * lv.nodes;
@@ -776,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, 
   // Rank-cut element of the composite (key, token) in ascending order.
   uint32_t kr = cut, prefix = 0, pmask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    const uint32_t d = radix_pass(keys, src, nd.start, nd.n, false, 0, prefix, pmask, shift, kr, hist, bcast);
+    const uint32_t d = radix_pass<NT>(keys, src, nd.start, nd.n, false, 0, prefix, pmask, shift, kr, hist, wsum, bcast);
     prefix |= d << shift;
     pmask |= 255u << shift;
   }
@@ -787,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, 
     prefix = 0;
     pmask = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      const uint32_t d = radix_pass(keys, src, nd.start, nd.n, true, thi, prefix, pmask, shift, kr, hist, bcast);
+      const uint32_t d = radix_pass<NT>(keys, src, nd.start, nd.n, true, thi, prefix, pmask, shift, kr, hist, wsum, bcast);
       prefix |= d << shift;
       pmask |= 255u << shift;
     }
@@ -798,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, 
   constexpr int E = 8;
   const int tid = threadIdx.x;
   uint32_t left_done = 0, right_done = 0;
-  for (int b = 0; b < nd.n; b += kThreads * E) {
+  for (int b = 0; b < nd.n; b += NT * E) {
     const int i0 = b + tid * E;
     int32_t tk[E];
     bool lf[E];
@@ -818,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void pddp_split_kernel(PddpArgs a, Ws w, 
     }
     uint32_t incl;
     const uint32_t packed = nl | (nr << 16);
-    const uint32_t tot = block_scan(packed, wsum, incl);
+    const uint32_t tot = block_scan<NT>(packed, wsum, incl);
     uint32_t pl = left_done + (incl & 0xffffu) - nl;
     uint32_t pr = right_done + (incl >> 16) - nr;
 #pragma unroll
@@ -852,33 +855,30 @@ hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int L = level_count(a.N, a.C);
-  const size_t lds = (size_t)(stats_region_floats<T, D>() + 3 * D + 8 + kThreads) * sizeof(float);
-  // The fp32 statistics and the power kernels hold a D x D covariance in LDS
-  // (64 KiB at D = 128), above the default dynamic-LDS limit.
-  if constexpr (!std::is_same<T, __bf16>::value) {
-    if ((e = hipFuncSetAttribute((const void*)pddp_stats_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds)) != hipSuccess)
-      return e;
-  }
-  if ((e = hipFuncSetAttribute((const void*)pddp_power_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds)) != hipSuccess)
-    return e;
+  const size_t lds_f32 = (size_t)stats_f32_lds_floats<T, D>() * sizeof(float);
+  const size_t lds_pow = (size_t)PowLds<D>::FLOATS * sizeof(float);
   for (int l = 0; l < L; ++l) {
     Level lv{l, 1 << l, parts_for(a.N, l)};
     const unsigned nb = (unsigned)(a.H * lv.nodes * lv.parts);
     if constexpr (std::is_same<T, __bf16>::value)
       hipLaunchKernelGGL((pddp_stats_bf16_kernel<D>), dim3(nb), dim3(kThreads), BStats<D>::BYTES, s, a, w, lv);
     else
-      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), lds, s, a, w, lv);
+      hipLaunchKernelGGL((pddp_stats_kernel<T, D>), dim3(nb), dim3(kThreads), lds_f32, s, a, w, lv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (lv.parts > 1) {
-      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), lds, s, a, w, lv);
+      hipLaunchKernelGGL((pddp_power_kernel<T, D>), dim3(a.H * lv.nodes), dim3(kThreads), lds_pow, s, a, w, lv);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((pddp_project_kernel<T, D>), dim3(nb), dim3(kThreads), 0, s, a, w, lv);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (lv.parts > 1) {  // single-block nodes project inside the statistics kernel
+      hipLaunchKernelGGL((pddp_project_kernel<T, D>), dim3(nb), dim3(kThreads), 0, s, a, w, lv);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if ((e = hipMemcpyAsync(w.tmp_perm, a.perm, total * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(pddp_split_kernel, dim3(a.H * lv.nodes), dim3(kThreads), 0, s, a, w, lv);
+    // few nodes (the top levels): 1024 threads per node
+    if (lv.nodes <= 4)
+      hipLaunchKernelGGL((pddp_split_kernel<1024>), dim3(a.H * lv.nodes), dim3(1024), 0, s, a, w, lv);
+    else
+      hipLaunchKernelGGL((pddp_split_kernel<kThreads>), dim3(a.H * lv.nodes), dim3(kThreads), 0, s, a, w, lv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
