@@ -35,15 +35,26 @@ struct QTile {
 };
 
 // Per-wave shared memory of the fused top-K: a 4096-bin histogram of the top 12
-// value bits and a candidate list (bit pattern, key id) of the histogram bin that
+// value bits, and a candidate list (bit pattern, key id) of the histogram bin that
 // holds the K-th largest mass.
 constexpr int kHistBins = 4096;
 constexpr int kCandCap = 2048;
-struct WaveLds {
-  uint32_t hist[kHistBins];
+struct WaveCand {
   uint32_t cand_bits[kCandCap];
   int32_t cand_id[kCandCap];
 };
+
+// LDS atomic add issued through inline asm.  The compiler cannot tell LDS that a
+// pending buffer_load ... lds copy writes from any other LDS, so before an
+// ordinary LDS atomic it waits for every such copy in flight; in the selection
+// loop that wait drained the whole K pipeline at every step.  The asm add is not
+// seen by that analysis.  LDS operations of a wave complete in order, so the
+// compiler's own lgkmcnt waits stay sufficient, and the histogram is read only
+// after an explicit s_waitcnt lgkmcnt(0).
+__device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)p;
+  asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
 
 // Ranks of this lane's flagged entries among the flagged entries of a 64 x 4
 // block ordered lane-major, then by j: rank[j] = flagged entries before (lane, j).
@@ -137,12 +148,12 @@ __device__ __forceinline__ void scan_row(const uint32_t* rb, int N, F&& f) {
 }
 
 // Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
-// id.  `w->hist` already holds the 12-bit histogram (bits 30..19) of the row.
-__device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out, WaveLds* w) {
+// id.  `hist` already holds the 12-bit histogram (bits 30..19) of the row.
+__device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out, uint32_t* hist, WaveCand* w) {
   const int lane = threadIdx.x & 63;
   const uint32_t* rb = reinterpret_cast<const uint32_t*>(row);
   uint32_t kr = (uint32_t)K, cnt = 0;
-  uint32_t prefix = pick_digit(w->hist, kHistBins, kr, cnt) << 19;
+  uint32_t prefix = pick_digit(hist, kHistBins, kr, cnt) << 19;
   uint32_t pmask = 0xfffu << 19;
   int shift = 19;
   // Refine the prefix while too many entries share it: bits 18..7, then 6..0.
@@ -152,7 +163,7 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
     const int nshift = shift >= 12 ? shift - 12 : 0;
     const int bins = 1 << (shift - nshift);
     const int hb = bins < 64 ? 64 : bins;
-    for (int j = lane; j < hb; j += 64) w->hist[j] = 0;
+    for (int j = lane; j < hb; j += 64) hist[j] = 0;
     __builtin_amdgcn_s_waitcnt(0);
     scan_row(rb, N, [&](int base, const uint32_t (&b)[kUnroll][4]) {
 #pragma unroll
@@ -161,11 +172,11 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
         for (int j = 0; j < 4; ++j) {
           const int i = base + 256 * u + 4 * lane + j;
           if (i < N && (b[u][j] & pmask) == prefix)
-            atomicAdd(&w->hist[(b[u][j] >> nshift) & (uint32_t)(bins - 1)], 1u);
+            atomicAdd(&hist[(b[u][j] >> nshift) & (uint32_t)(bins - 1)], 1u);
         }
     });
     __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t d = pick_digit(w->hist, hb, kr, cnt);
+    const uint32_t d = pick_digit(hist, hb, kr, cnt);
     prefix |= d << nshift;
     pmask |= (uint32_t)(bins - 1) << nshift;
     shift = nshift;
@@ -199,14 +210,14 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
   while (shift > 0) {
     const int nshift = shift >= 8 ? shift - 8 : 0;
     const int bins = 1 << (shift - nshift);
-    for (int j = lane; j < 256; j += 64) w->hist[j] = 0;
+    for (int j = lane; j < 256; j += 64) hist[j] = 0;
     __builtin_amdgcn_s_waitcnt(0);
     for (uint32_t c = lane; c < nc; c += 64) {
       const uint32_t b = w->cand_bits[c];
-      if ((b & pmask) == prefix) atomicAdd(&w->hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
+      if ((b & pmask) == prefix) atomicAdd(&hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
     }
     __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t d = pick_digit(w->hist, 256, kr, cnt);
+    const uint32_t d = pick_digit(hist, 256, kr, cnt);
     prefix |= d << nshift;
     pmask |= (uint32_t)(bins - 1) << nshift;
     shift = nshift;
@@ -250,7 +261,8 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
 template <typename T, int D>
 __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   using TL = QTile<T, D>;
-  extern __shared__ WaveLds wlds[];
+  __shared__ uint32_t s_hist[4][kHistBins];
+  extern __shared__ WaveCand wcand[];
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int hf = lane >> 5, lm = lane & 31;
   const int items = a.hcount * a.G;
@@ -258,7 +270,8 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   if (blk < 0) return;
   const int item = blk * 4 + wid;
   if (item >= items) return;  // no block-level synchronisation below
-  WaveLds* w = &wlds[wid];
+  WaveCand* w = &wcand[wid];
+  uint32_t* hist = s_hist[wid];
   const int hl = item / a.G, g = item - hl * a.G;
   const int h = a.h0 + hl;
   const int N = a.N;
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   const uint32_t head_bytes = (uint32_t)((size_t)N * TL::ROWB);
   const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
   const auto rk = make_rsrc((const char*)a.k + head_off, head_bytes);
-  for (int j = lane; j < kHistBins; j += 64) w->hist[j] = 0;
+  for (int j = lane; j < kHistBins; j += 64) hist[j] = 0;
 
   // Query rows of this group: lane lm holds queries lm and lm + 32 (A operand).
   int tokq[2];
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
     acc = pair_sum(acc);
     if (hf == 0 && t0 + lm < N) {
       out[t0 + lm] = acc;
-      atomicAdd(&w->hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
+      atomicAdd(&hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
     }
   };
   // Software pipeline: the MFMAs of step i+1 are issued before the exponentials
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   // never read before, so loads issued after the wait see the stored values.
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, w);
+  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, hist, w);
 }
 
 // bf16 pass 2 with K staged through LDS.  Every group scans all keys in the
@@ -386,6 +399,12 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
 // and one block barrier per step separates "copies landed / previous tile
 // consumed" from the reads.  This cuts the address work of the K fetches by
 // 16x (quad-contiguous copies, a quarter each) and the L2 traffic by 4x.
+//
+// With one block per CU, the copies in flight set the pace: two 8 KiB stages
+// held the loop at about 4 TB/s of K, at the copy latency, whatever the math.
+// So the tiles rotate through NS = 6 stages, copied NS steps ahead: two stages
+// after the candidate areas, and one in each wave's top-K candidate area (free
+// until the loop ends).
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void group_mass_lds_kernel(MassArgs a) {
@@ -399,16 +418,22 @@ void group_mass_lds_kernel(MassArgs a) {
   const int hl = blk / gb;
   const int g = (blk - hl * gb) * 4 + wid;
   const bool active = g < a.G;  // a wave past the last group only helps copy
-  WaveLds* w = (WaveLds*)smem + wid;
-  LDSP char* s0 = (LDSP char*)(smem + 4 * sizeof(WaveLds));
-  LDSP char* s1 = s0 + L::TILE;
+  uint32_t* hist = (uint32_t*)smem + wid * kHistBins;
+  WaveCand* w = (WaveCand*)(smem + 4 * kHistBins * sizeof(uint32_t)) + wid;
+  LDSP char* lbase = (LDSP char*)smem + 4 * kHistBins * sizeof(uint32_t);
+  constexpr int NS = 6;
+  static_assert(sizeof(WaveCand) >= (size_t)L::TILE, "a K tile fits a candidate area");
+  // stage j: two after the candidate areas, then the candidate area of wave j - 2
+  auto stage = [&](int j) -> LDSP char* {
+    return lbase + (j < 2 ? 4 * (int)sizeof(WaveCand) + j * L::TILE : (j - 2) * (int)sizeof(WaveCand));
+  };
   const int h = a.h0 + hl;
   const int N = a.N;
   const size_t head_off = (size_t)h * N * L::ROWB;
   const uint32_t head_bytes = (uint32_t)((size_t)N * L::ROWB);
   const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
   const auto rk = make_rsrc((const char*)a.k + head_off, head_bytes);
-  for (int j = lane; j < kHistBins; j += 64) w->hist[j] = 0;
+  for (int j = lane; j < kHistBins; j += 64) hist[j] = 0;
 
   // Query rows of this group: lane lm holds queries lm and lm + 32 (A operand).
   int tokq[2];
@@ -488,50 +513,58 @@ void group_mass_lds_kernel(MassArgs a) {
     uint32_t soff = keep ? (uint32_t)(t0 + lm) * 4u : 0xfffffff0u;
     asm volatile("" : "+v"(soff));  // opaque: keeps the store out of the branch on `keep`
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rout, soff, 0, 0);
-    if (keep) atomicAdd(&w->hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
+    if (keep) lds_add_u32(&hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
   };
   // Iteration i: barrier (every wave's copy of K(i+1) landed, every wave done
-  // with K(i)'s stage), copy K(i+2) into that stage, QK of step i+1, then the
-  // exponentials of step i (they overlap the MFMAs).  K(j) lives in stage j % 2.
-  auto iter = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], LDSP char* sp, LDSP char* sq, int i) {
+  // with K(i)'s stage), copy K(i+NS) into that stage, QK of step i+1, then the
+  // exponentials of step i (they overlap the MFMAs).  K(j) lives in stage j % NS.
+  // Copies run past the last step (those rows read as zeros and are never used),
+  // so every iteration issues NC copies and one store, and the number of vector
+  // memory operations issued after this wave's copy of K(i+1) is fixed: the
+  // copies of the NS - 2 steps after it (from the prologue, or one iteration
+  // each), plus one store per iteration since the prologue, at most NS - 1.
+  auto iter = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int i) {
     __builtin_amdgcn_sched_barrier(0);
-    // this wave's copies of K(i+1) came before the one mass store of step i-1:
-    // everything but that store must have landed (a store's completion is not
-    // needed here, and waiting for it would expose the write latency every step)
-    wait_vm<1>();
+    if (i >= NS - 1)
+      wait_vm<(NS - 2) * NC + NS - 1>();
+    else
+      wait_vm<(NS - 2) * NC>();  // fewer stores so far: wait a little longer
     block_barrier();
-    if (i + 2 < nsteps) tile_copy_dense<D, NC>(sp, rk, i + 2, ebase, goff, wid * NC);
+    tile_copy_dense<D, NC>(stage(i % NS), rk, i + NS, ebase, goff, wid * NC);
     __builtin_amdgcn_sched_barrier(0);
-    qk(sn, sq);
+    qk(sn, stage((i + 1) % NS));
     reduce_store(sc, i * 32);
   };
   f32x16 sa[2], sb[2];
-  tile_copy_dense<D, NC>(s0, rk, 0, ebase, goff, wid * NC);
-  if (nsteps > 1) tile_copy_dense<D, NC>(s1, rk, 1, ebase, goff, wid * NC);
-  wait_vm<0>();
+  for (int j = 0; j < NS; ++j) tile_copy_dense<D, NC>(stage(j), rk, j, ebase, goff, wid * NC);
+  wait_vm<(NS - 1) * NC>();
   block_barrier();
-  qk(sa, s0);
+  qk(sa, stage(0));
   int it = 0;
   for (; it + 2 < nsteps; it += 2) {
-    iter(sa, sb, s0, s1, it);
-    iter(sb, sa, s1, s0, it + 1);
+    iter(sa, sb, it);
+    iter(sb, sa, it + 1);
   }
   if (it + 1 < nsteps) {
-    iter(sa, sb, s0, s1, it);
+    iter(sa, sb, it);
     reduce_store(sb, (it + 1) * 32);
   } else {
     reduce_store(sa, it * 32);
   }
+  // The copies past the last step land, and every wave is done with the stages,
+  // before the candidate areas are written (or the block's LDS is released).
+  wait_vm<0>();
+  block_barrier();
   if (!active) return;  // no block-level synchronisation below
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, w);
+  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, hist, w);
 }
 
 template <int D>
 hipError_t launch_mass_lds(const MassArgs& a, hipStream_t s) {
   const int blocks = xcd_grid(a.hcount * ((a.G + 3) / 4));
-  const size_t lds = 4 * sizeof(WaveLds) + 2 * LT<D>::TILE;
+  const size_t lds = 4 * (kHistBins * sizeof(uint32_t) + sizeof(WaveCand)) + 2 * LT<D>::TILE;
   hipError_t e = hipFuncSetAttribute((const void*)group_mass_lds_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -543,7 +576,7 @@ template <typename T, int D>
 hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   const int items = a.hcount * a.G;
   const int blocks = xcd_grid((items + 3) / 4);
-  const size_t lds = 4 * sizeof(WaveLds);
+  const size_t lds = 4 * sizeof(WaveCand);  // + the static histograms
   hipError_t e = hipFuncSetAttribute((const void*)group_mass_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
