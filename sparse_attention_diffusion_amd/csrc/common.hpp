@@ -94,23 +94,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Wave sum on DPP and permlane swaps (no LDS round trips).  Every step adds two
-// partners whose values are each already uniform over their own half, and IEEE
-// addition is commutative, so all 64 lanes end with the same bits.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-  x += dpp_mov<0x141>(x);  // row_half_mirror: quad 0 <-> quad 1 of each 8 lanes
-  x += dpp_mov<0x140>(x);  // row_mirror: the two halves of each 16-lane row
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // rows 0 <-> 1, 2 <-> 3
-  return pair_sum(x);                                 // the two 32-lane halves
-}
-
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own 4 MB L2), and
 // all XCDs share the MALL.  Map hardware block b (XCD b % 8, local slot b / 8) so
 // that each XCD runs `chunk` consecutive logical blocks at a time while the 8 XCDs

@@ -109,6 +109,23 @@ inline Ws carve(void* base, int H, int N, int D, int C) {
 template <typename T>
 __device__ __forceinline__ float ldf(const T* p) { return (float)*p; }
 
+// Wave sum on DPP and permlane swaps (no LDS round trips).  Every step adds two
+// partners whose values are each already uniform over their own half, and IEEE
+// addition is commutative, so all 64 lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_mov<0x141>(x);  // row_half_mirror: quad 0 <-> quad 1 of each 8 lanes
+  x += dpp_mov<0x140>(x);  // row_mirror: the two halves of each 16-lane row
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // rows 0 <-> 1, 2 <-> 3
+  return pair_sum(x);                                 // the two 32-lane halves
+}
+
 // Accumulated statistics of one block: fp32 MFMA tiles of S = sum (x - r)(x - r)^T.
 // D = 128: 4 x 4 tiles of 32 x 32, wave w owns tile row w; D = 64: 2 x 2, one per wave.
 template <typename T, int D>
