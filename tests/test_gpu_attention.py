@@ -150,3 +150,30 @@ def test_large_logits_are_stable():
     torch.cuda.synchronize()
     assert_close(host(o)[0], ref.sparse_attention(q[0], kk[0], v[0], perm[0], idx[0][:, :k], 64, s), 1e-4, 1e-5)
     assert_close(host(o_d)[0], ref.dense_attention(q[0], kk[0], v[0], s), 1e-4, 1e-5)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_bf16_overflowing_logit_takes_the_online_path(d):
+    # One key sits far above every logit of the first 32-key step for the first 32
+    # queries only, so their row sums overflow the fixed softmax offset (first-step
+    # maximum + 16, log2 units) and that half of group 0 is redone with the online
+    # pass, while the other half of the same group and every other group keep the
+    # LDS path.  n = 200 also leaves the last group partly empty.
+    h, n = 1, 200
+    r = np.random.default_rng(d)
+    q = 0.1 * r.standard_normal((h, n, d))
+    kk = 0.1 * r.standard_normal((h, n, d))
+    v = r.standard_normal((h, n, d))
+    q[0, :32, :] += 4.0
+    kk[0, 150, :] = 4.0
+    q, kk, v = (W.store(x, "bf16") for x in (q, kk, v))
+    s = 1.0 / np.sqrt(d)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(kk, "bf16"), to_dev(v, "bf16")
+    o, lse = mcs.mcs_dense_attn(qd, kd, vd, want_lse=True)
+    perm, idx = random_groups(n, n, h, seed=d)
+    o_s = mcs.mcs_sparse_attn(qd, kd, vd, torch.from_numpy(perm).to(dev()), torch.from_numpy(idx).to(dev()), n)
+    torch.cuda.synchronize()
+    want = ref.dense_attention(q[0], kk[0], v[0], s)
+    assert_close(host(o)[0], want, 2e-2, 2e-3, f"dense d{d}")
+    assert_close(host(lse)[0], ref.row_lse(q[0], kk[0], s), 2e-4, 3e-5, f"lse d{d}")
+    assert_close(host(o_s)[0], want, 2e-2, 2e-3, f"sparse K=N d{d}")
