@@ -16,7 +16,10 @@ One timed step is one pass of the whole hot path over that layer:
 launch stream); `x_vs_dense` compares with this library's own dense attention on
 the same tensors.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--density RHO] [--cold]
+
+--cold writes a 512 MB scratch buffer (twice the 256 MB MALL) before every timed
+call, outside its events, so each stage starts with cold caches.
 """
 from __future__ import annotations
 
@@ -111,7 +114,29 @@ def cpu_baseline(q, k, v, perm, idx, kk, scale, budget_s=12.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
             "sample": f"fp64 numpy gather-sparse attention of {done} query groups (64 queries x {kk} keys x "
-                      f"D={d}) of head 0, {dt:.1f} s"}
+                      f"D={d}) of head 0, {dt:.1f} s; host {_host_info(cores)}"}
+
+
+def _host_info(cores: int) -> str:
+    """CPU model, usable cores and BLAS threads of the machine running the oracle."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "?"
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            blas = f"{pools[0].get('internal_api')} x{pools[0].get('num_threads')}"
+    except Exception:  # threadpoolctl missing or failing: leave it unknown
+        pass
+    return f"{model}, {cores} usable cores, BLAS {blas}"
 
 
 def sdpa_context(q, k, v, reps=3):
@@ -141,6 +166,8 @@ def main():
     ap.add_argument("--density", type=float, default=0.2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sdpa", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MB scratch buffer before every timed call (cold L2 and MALL)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy 1 GiB once before the workload (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -184,18 +211,25 @@ def main():
     o_dense = torch.empty_like(q)
     lse = torch.empty((h, n), dtype=torch.float32, device=dev)
 
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    def timed(fn):
+        if scratch is not None:
+            scratch.fill_(1)  # same stream, before the start event: not timed
+        return _timed(fn, stream)
+
     def step(record):
         ev = {}
         # anchor (composite entry point), then its stages one by one for the breakdown
-        _, ev["anchor"] = _timed(lambda: mcs.mcs_anchor(q, k, v, kk, ws=ws, out=cache), stream)
-        _, ev["group"] = _timed(lambda: mcs.mcs_group(q, ws=gws, perm=cache["perm"]), stream)
-        _, ev["dense"] = _timed(lambda: mcs.mcs_dense_attn(q, k, v, want_lse=False, o=o_dense), stream)
-        _, ev["select"] = _timed(lambda: mcs.mcs_select(q, k, cache["perm"], kk, lse=None, ws=ws[:swsz],
-                                                        idx=cache["idx"]), stream)
-        _, ev["reuse"] = _timed(lambda: mcs.mcs_reuse(q, k, v, cache["perm"], cache["idx"], cache["resid"], kk,
-                                                      o=o_reuse), stream)
-        _, ev["sparse"] = _timed(lambda: mcs.mcs_sparse_attn(q, k, v, cache["perm"], cache["idx"], kk,
-                                                             o=o_sparse), stream)
+        _, ev["anchor"] = timed(lambda: mcs.mcs_anchor(q, k, v, kk, ws=ws, out=cache))
+        _, ev["group"] = timed(lambda: mcs.mcs_group(q, ws=gws, perm=cache["perm"]))
+        _, ev["dense"] = timed(lambda: mcs.mcs_dense_attn(q, k, v, want_lse=False, o=o_dense))
+        _, ev["select"] = timed(lambda: mcs.mcs_select(q, k, cache["perm"], kk, lse=None, ws=ws[:swsz],
+                                                       idx=cache["idx"]))
+        _, ev["reuse"] = timed(lambda: mcs.mcs_reuse(q, k, v, cache["perm"], cache["idx"], cache["resid"], kk,
+                                                     o=o_reuse))
+        _, ev["sparse"] = timed(lambda: mcs.mcs_sparse_attn(q, k, v, cache["perm"], cache["idx"], kk,
+                                                            o=o_sparse))
         if record is not None:
             record.append(ev)
 
@@ -216,7 +250,13 @@ def main():
     t_sparse, t_dense = ms["sparse"] / 1e3, ms["dense"] / 1e3
     value = flops_sparse / t_sparse / 1e12
     speedup = t_dense / t_sparse
-    # PDDP / selection bandwidth reference counts (per layer): see the design doc
+    # Reference work of the other stages (per layer):
+    #   PDDP: per level of the split tree, two reads of Q (statistics, projections)
+    #         plus ~6 4-byte scalars per token (perm, keys, partition);
+    #   selection: two N^2 D contractions (pass 1 LSE, pass 2 group mass).
+    levels = max(1, (g - 1).bit_length())
+    pddp_bytes = levels * (2.0 * n * d * h * q.element_size() + 24.0 * n * h)
+    flops_select = 4.0 * n * n * d * h
     sdpa_ms = None if args.no_sdpa else sdpa_context(q, k, v)
     out = {
         "metric": "gather-sparse attn TFLOP/s, % MFMA peak, x vs dense @ density 0.2, 75,600 tok",
@@ -239,6 +279,12 @@ def main():
         "pct_of_ideal": round(100.0 * pct_of_ideal(speedup, args.density), 1),
         "dense_tflops": round(flops_dense / t_dense / 1e12, 2),
         "stage_ms": {key: round(val, 3) for key, val in ms.items()},
+        "cache": "cold (512 MB written before every timed call)" if args.cold else "warm",
+        "stage_rates": {"group_ref_gbps": round(pddp_bytes / (ms["group"] / 1e3) / 1e9, 1),
+                        "group_ref_frac_hbm": round(pddp_bytes / (ms["group"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "select_tflops": round(flops_select / (ms["select"] / 1e3) / 1e12, 1),
+                        "select_frac_mfma": round(flops_select / (ms["select"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                                  4)},
         "torch_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
