@@ -44,3 +44,34 @@ def test_wan14b_720p_sampled_parity():
     rep = ref.pddp_verify(host(q[5]), host(out["perm"][5]), 64)
     print(f"pddp verify head 5: {rep}")
     assert rep["bad"] == 0
+
+
+def test_hunyuan13b_720p_sampled_parity():
+    # 118,800 tokens, 24 heads, density 0.15: grouping, selection and sparse
+    # attention of the anchor, checked on sampled groups and one whole head.
+    wl = W.WORKLOADS["hunyuan13b_720p"]
+    dev = torch.device("cuda:0")
+    kk = wl.topk(0.15)
+    q, k, v = W.make_qkv_torch(wl, dev)
+    out = mcs.mcs_anchor(q, k, v, kk, heads_per_pass=8)
+    torch.cuda.synchronize()
+    s = 1.0 / np.sqrt(wl.head_dim)
+    rng = np.random.default_rng(1)
+    h = 17
+    qh, khh, vh = (host(t[h]) for t in (q, k, v))
+    perm = host(out["perm"][h])
+    idx = host(out["idx"][h])
+    assert sorted(perm.tolist()) == list(range(wl.n))
+    for g in sorted(set(rng.choice(wl.groups, 2, replace=False).tolist()) | {wl.groups - 1}):
+        mem = perm[g * 64:(g + 1) * 64]
+        lse = np.zeros(wl.n)
+        lse[mem] = ref.row_lse(qh, khh, s, rows=mem)
+        mass = ref.group_mass(qh, khh, lse, perm, 64, s, groups=[g])[0]
+        check_index_row(idx[g], mass, kk, wl.n)
+        want_d = ref.dense_attention(qh, khh, vh, s, rows=mem)
+        want_s = ref.sparse_attention_group(qh, khh, vh, mem, idx[g][:kk].astype(np.int64), s)
+        assert_close(host(out["o_dense"][h])[mem], want_d, what=f"dense g{g}")
+        assert_close(host(out["resid"][h])[mem], want_d - want_s, what=f"resid g{g}")
+    rep = ref.pddp_verify(qh, perm, 64)
+    print(f"pddp verify head {h}: {rep}")
+    assert rep["bad"] == 0
