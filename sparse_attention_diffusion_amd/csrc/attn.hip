@@ -452,7 +452,7 @@ __device__ __forceinline__ void state_init(State<T, D, PV>& st) {
 
 // Row statistics, normalisation and the epilogue stores of one group.
 template <typename T, int D, int EPI, bool PV>
-__device__ __forceinline__ void finish(const State<T, D, PV>& st, const AttnArgs& a, int h, int g, const int (&tokq)[2],
+__device__ __forceinline__ void finish(const State<T, D, PV>& st, const AttnArgs& a, int h, const int (&tokq)[2],
                                        const bool (&qvalid)[2], int lm, int hf) {
   using TL = Tile<T, D>;
   const int N = a.N;
@@ -561,9 +561,9 @@ void attn_kernel(AttnArgs a) {
     State<T, D, PV> so;
     state_init<T, D, PV>(so);
     pass_online<T, D, GATHER, PV>(so, x, rq, tokq[0], tokq[1]);
-    finish<T, D, EPI, PV>(so, a, h, g, tokq, qvalid, lm, hf);
+    finish<T, D, EPI, PV>(so, a, h, tokq, qvalid, lm, hf);
   } else {
-    finish<T, D, EPI, PV>(st, a, h, g, tokq, qvalid, lm, hf);
+    finish<T, D, EPI, PV>(st, a, h, tokq, qvalid, lm, hf);
   }
 }
 
@@ -986,7 +986,7 @@ void attn_lds_kernel(AttnArgs a) {
     State<__bf16, D, PV> so;
     state_init<__bf16, D, PV>(so);
     pass_online<__bf16, D, GATHER, PV>(so, xo, rq, tokq[0], tokq[1]);
-    finish<__bf16, D, EPI, PV>(so, a, h, g, tokq, qvalid, lm, hf);
+    finish<__bf16, D, EPI, PV>(so, a, h, tokq, qvalid, lm, hf);
   } else {
     lfinish<D, EPI, PV>(st, a, h, tokq, qvalid, lane, s0);
   }

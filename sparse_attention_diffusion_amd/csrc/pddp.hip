@@ -34,7 +34,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxParts = 64;  // blocks per node at the top levels
-constexpr int kTileRows = 32;  // rows staged in LDS per stats iteration
 
 struct Node {
   int start, n;
@@ -93,7 +92,7 @@ inline int parts_for(int N, int level) {
   return p < 1 ? 1 : p;
 }
 
-inline Ws carve(void* base, int H, int N, int D, int C) {
+inline Ws carve(void* base, int H, int N, int D) {
   char* p = (char*)base;
   Ws w;
   w.tmp_perm = (int32_t*)p;
@@ -537,7 +536,7 @@ void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
   const int ntiles = r1 > r0 ? (r1 - r0 + B::TR - 1) / B::TR : 0;
   const bf16* qh = (const bf16*)a.q + (size_t)h * a.N * D;
   const int32_t* permh = a.perm + (size_t)h * a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   LDSP char* lds = (LDSP char*)smem;
 
   // Staging: thread tid converts chunk c of rows rbase + RSTEP*j of each tile.
@@ -866,7 +865,7 @@ __global__ void iota_kernel(int32_t* perm, int H, int N) {
 
 template <typename T, int D>
 hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
-  Ws w = carve(a.ws, a.H, a.N, D, a.C);
+  Ws w = carve(a.ws, a.H, a.N, D);
   const size_t total = (size_t)a.H * a.N;
   hipLaunchKernelGGL(iota_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.perm, a.H, a.N);
   hipError_t e = hipGetLastError();
