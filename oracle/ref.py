@@ -298,3 +298,41 @@ def reuse(q, k, v, perm, idx, resid, group, scale, groups=None):
     groups and indices, plus the cached residual (no regrouping, no reselection)."""
     o = sparse_attention(q, k, v, perm, idx, group, scale, groups)
     return o + _f64(resid)
+
+
+# ---------------------------------------------------------------------------
+# Compact kept-key sets of the meta-cache (residual paragraph: cached indices
+# move to host memory; their size sets the host-link traffic)
+# ---------------------------------------------------------------------------
+
+def idx_to_bits(idx_rows, n, topk):
+    """Kept-key lists -> bitmaps: row r of the result has ceil(n/32) uint32
+    words; bit b of word w is set when key 32*w + b is among the first `topk`
+    entries of idx_rows[r] (entries outside [0, n) are ignored)."""
+    idx_rows = np.asarray(idx_rows)
+    words = (n + 31) // 32
+    out = np.zeros(idx_rows.shape[:-1] + (words,), dtype=np.uint32)
+    flat_idx = idx_rows.reshape(-1, idx_rows.shape[-1])
+    flat_out = out.reshape(-1, words)
+    for r in range(flat_idx.shape[0]):
+        for key in flat_idx[r, :topk]:
+            key = int(key)
+            if 0 <= key < n:
+                flat_out[r, key // 32] |= np.uint32(1 << (key % 32))
+    return out
+
+
+def bits_to_idx(bits_rows, n, topk, kpad):
+    """Bitmaps -> kept-key lists: the keys of the set bits below n in ascending
+    order, at most `topk` of them, then -1 up to kpad."""
+    bits_rows = np.asarray(bits_rows, dtype=np.uint32)
+    words = bits_rows.shape[-1]
+    out = np.full(bits_rows.shape[:-1] + (kpad,), -1, dtype=np.int32)
+    flat_bits = bits_rows.reshape(-1, words)
+    flat_out = out.reshape(-1, kpad)
+    for r in range(flat_bits.shape[0]):
+        keys = [32 * w + b for w in range(words) for b in range(32)
+                if (int(flat_bits[r, w]) >> b) & 1 and 32 * w + b < n]
+        keys = keys[:topk]
+        flat_out[r, :len(keys)] = keys
+    return out
