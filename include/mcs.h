@@ -137,6 +137,26 @@ int mcs_anchor(const mcs_dims* d, const void* q, const void* k, const void* v, i
 int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
               const int32_t* idx, const void* resid, void* o, hipStream_t stream);
 
+/* Compact kept-key sets for the meta-cache (summary page, residual paragraph:
+ * the residual-plus-index traffic of offloaded entries must hide behind
+ * compute).  bits: uint32 [H][G][W], W = ceil(N/32); bit b of word w of row
+ * (h, g) is set when key 32*w + b is in that group's kept set.  About N/8 bytes
+ * per group instead of 4*kpad.
+ *
+ * mcs_idx_to_bits: encode idx (the first K entries of every row; entries
+ * outside [0, N) are ignored) into bits.  Every word of bits is written.
+ * mcs_bits_to_idx: decode bits into idx: the set bits of each row as ascending
+ * key ids, then -1 up to kpad.  A row with more than K set bits keeps its K
+ * lowest keys; one with fewer is -1 padded from its last key on (a bitmap from
+ * mcs_idx_to_bits of a list with K distinct keys has exactly K).
+ * Both: d gives heads, n, group (64), topk and kpad as for idx; head_dim,
+ * dtype and scale must hold valid values but are not used.  N <=
+ * MCS_BITS_MAX_N (MCS_EUNSUPPORTED otherwise); idx and bits 4-byte aligned;
+ * bounded by HBM bandwidth. */
+#define MCS_BITS_MAX_N (1 << 20)
+int mcs_idx_to_bits(const mcs_dims* d, const int32_t* idx, uint32_t* bits, hipStream_t stream);
+int mcs_bits_to_idx(const mcs_dims* d, const uint32_t* bits, int32_t* idx, hipStream_t stream);
+
 /* Meta-cache transfer helper (summary page, residual paragraph: inactive cache
  * entries move to host memory and the next layer is prefetched): enqueue a copy
  * of `bytes` bytes on `stream` (kind MCS_COPY_H2D / D2H / D2D; host buffers

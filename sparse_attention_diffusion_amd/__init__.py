@@ -169,6 +169,56 @@ def mcs_reuse(q, k, v, perm, idx, resid, topk: int, o=None):
     return o
 
 
+def bits_words(n: int) -> int:
+    """Words per row of a key bitmap: ceil(n / 32)."""
+    return (n + 31) // 32
+
+
+def _check_rows(t, n, g, shape=None):
+    """One row per (head, group): g must be ceil(n / 64); int32 storage."""
+    torch = _torch()
+    if t.dtype != torch.int32 or t.dim() != 3:
+        raise ValueError("key lists and bitmaps are int32 [H, G, width]")
+    if g != -(-n // GROUP):
+        raise ValueError(f"{g} groups do not match n={n} (expected {-(-n // GROUP)})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"shape {tuple(t.shape)} differs from {tuple(shape)}")
+
+
+def mcs_idx_to_bits(idx, n: int, topk: int, bits=None):
+    """Kept-key lists int32 [H, G, kpad] -> key bitmaps uint32 (stored as int32) [H, G, ceil(n/32)]."""
+    torch = _torch()
+    lib = _abi.load()
+    h, g, kpad = idx.shape
+    _check_rows(idx, n, g)
+    d = McsDims(heads=h, n=n, head_dim=128, group=GROUP, topk=topk, kpad=kpad, dtype=MCS_BF16,
+                power_iters=POWER_ITERS, scale=1.0)
+    if bits is None:
+        bits = torch.empty((h, g, bits_words(n)), dtype=torch.int32, device=idx.device)
+    _check_rows(bits, n, g, (h, g, bits_words(n)))
+    _abi.check(lib.mcs_idx_to_bits(ctypes.byref(d), _ptr(idx), _ptr(bits), _stream(idx.device)))
+    return bits
+
+
+def mcs_bits_to_idx(bits, n: int, topk: int, idx=None, kpad: int | None = None):
+    """Key bitmaps [H, G, ceil(n/32)] -> kept-key lists int32 [H, G, kpad] (ascending, -1 padded)."""
+    torch = _torch()
+    lib = _abi.load()
+    h, g, _ = bits.shape
+    _check_rows(bits, n, g, (h, g, bits_words(n)))
+    if idx is not None:
+        kpad = idx.shape[2]
+    elif kpad is None:
+        kpad = kpad_for(topk)
+    d = McsDims(heads=h, n=n, head_dim=128, group=GROUP, topk=topk, kpad=kpad, dtype=MCS_BF16,
+                power_iters=POWER_ITERS, scale=1.0)
+    if idx is None:
+        idx = torch.empty((h, g, kpad), dtype=torch.int32, device=bits.device)
+    _check_rows(idx, n, g, (h, g, kpad))
+    _abi.check(lib.mcs_bits_to_idx(ctypes.byref(d), _ptr(bits), _ptr(idx), _stream(bits.device)))
+    return idx
+
+
 def mcs_copy_async(dst, src, kind: int, stream=None, event=None):
     """Enqueue a byte copy of src into dst on `stream` (default: current) and record `event`."""
     torch = _torch()

@@ -14,7 +14,9 @@ MCS_COPY_H2D, MCS_COPY_D2H, MCS_COPY_D2D = 1, 2, 3
 ABI_VERSION = 1
 
 EXPORTED = ("mcs_abi_version", "mcs_last_error", "mcs_workspace_bytes", "mcs_group", "mcs_select",
-            "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_reuse", "mcs_copy_async")
+            "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_reuse", "mcs_idx_to_bits", "mcs_bits_to_idx",
+            "mcs_copy_async")
+BITS_MAX_N = 1 << 20
 
 
 class McsDims(ctypes.Structure):
@@ -53,6 +55,8 @@ def load():
         "mcs_sparse_attn": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
         "mcs_anchor": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, S, St]),
         "mcs_reuse": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
+        "mcs_idx_to_bits": (ctypes.c_int, [D, P, P, St]),
+        "mcs_bits_to_idx": (ctypes.c_int, [D, P, P, St]),
         "mcs_copy_async": (ctypes.c_int, [P, P, S, I32, St, P]),
     }
     for name, (res, args) in sig.items():

@@ -1,4 +1,5 @@
-"""Meta-cache of the MC-Sparse hot path: per-layer {perm, idx, resid}.
+"""Meta-cache of the MC-Sparse hot path: per-layer {perm, idx, resid} (or, compact,
+{perm, bits, resid} with the kept-key lists as per-group key bitmaps).
 
 MC-Sparse summary page, residual paragraph: groups, indices and the residual are
 produced together on anchor steps and reused on later steps; when GPU memory is
@@ -73,24 +74,25 @@ class TorchBackend:
 
 
 class MetaCache:
-    """Per-layer cache of (perm, idx, resid) with optional host offload."""
-
-    KEYS = ("perm", "idx", "resid")
+    """Per-layer cache of named device tensors (perm, idx or bits, resid) with
+    optional host offload."""
 
     def __init__(self, layers, shapes, backend, offload=False, device_slots=2):
-        """shapes: {"perm": (shape, dtype), "idx": (...), "resid": (...)} of one layer."""
+        """shapes: {name: (shape, dtype)} of one layer's entry, e.g. {"perm": ...,
+        "idx": ..., "resid": ...}."""
         self.layers = layers
         self.shapes = shapes
+        self.keys = tuple(shapes)
         self.be = backend
         self.offload = offload
         nslots = min(layers, device_slots) if offload else layers
         if offload and nslots < 2 and layers > 1:
             raise ValueError("offload needs at least two device slots")
-        self.slots = [_Slot({k: backend.empty_device(*shapes[k]) for k in self.KEYS}) for _ in range(nslots)]
+        self.slots = [_Slot({k: backend.empty_device(*shapes[k]) for k in self.keys}) for _ in range(nslots)]
         self.entries = [_Entry() for _ in range(layers)]
         if offload:
             for e in self.entries:
-                e.host = {k: backend.empty_host(*shapes[k]) for k in self.KEYS}
+                e.host = {k: backend.empty_host(*shapes[k]) for k in self.keys}
         self.bytes_d2h = 0
         self.bytes_h2d = 0
 
@@ -150,7 +152,7 @@ class MetaCache:
         written = self.be.event()
         self.be.record(written, self.be.compute_stream())
         self.be.wait(self.be.side, written)
-        for k in self.KEYS:
+        for k in self.keys:
             self.be.copy(e.host[k], s.tensors[k], MCS_COPY_D2H, self.be.side)
             self.bytes_d2h += s.tensors[k].numel() * s.tensors[k].element_size()
         e.d2h_done = self.be.event()
@@ -174,7 +176,7 @@ class MetaCache:
         if s.released is not None:  # the compute stream's last use of the slot must be over
             self.be.wait(self.be.side, s.released)
         self.be.wait(self.be.side, e.d2h_done)
-        for k in self.KEYS:
+        for k in self.keys:
             self.be.copy(s.tensors[k], e.host[k], MCS_COPY_H2D, self.be.side)
             self.bytes_h2d += s.tensors[k].numel() * s.tensors[k].element_size()
         s.side_last = self.be.event()

@@ -286,6 +286,28 @@ int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, co
   return mcs_sparse_attn(d, q, k, v, perm, idx, resid, o, stream);
 }
 
+int mcs_idx_to_bits(const mcs_dims* d, const int32_t* idx, uint32_t* bits, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(idx, 4, "idx"));
+  CHECK(check_ptr(bits, 4, "bits"));
+  if (d->n > MCS_BITS_MAX_N) return fail(MCS_EUNSUPPORTED, "n %d above %d for key bitmaps", d->n, MCS_BITS_MAX_N);
+  hipError_t e = mcs::launch_idx_to_bits(idx, bits, d->heads * groups_of(d), d->n, d->topk, d->kpad, stream);
+  if (e != hipSuccess) return hip_fail(e, "key bitmap encode launch");
+  return MCS_OK;
+}
+
+int mcs_bits_to_idx(const mcs_dims* d, const uint32_t* bits, int32_t* idx, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(bits, 4, "bits"));
+  CHECK(check_ptr(idx, 4, "idx"));
+  if (d->n > MCS_BITS_MAX_N) return fail(MCS_EUNSUPPORTED, "n %d above %d for key bitmaps", d->n, MCS_BITS_MAX_N);
+  hipError_t e = mcs::launch_bits_to_idx(bits, idx, d->heads * groups_of(d), d->n, d->topk, d->kpad, stream);
+  if (e != hipSuccess) return hip_fail(e, "key bitmap decode launch");
+  return MCS_OK;
+}
+
 int mcs_copy_async(void* dst, const void* src, size_t bytes, int32_t kind, hipStream_t stream, hipEvent_t done) {
   g_err.clear();
   if (!dst || !src) return fail(MCS_EINVAL, "dst/src is NULL");

@@ -60,4 +60,10 @@ struct PddpArgs {
 size_t pddp_workspace_bytes(int H, int N, int D, int C);
 hipError_t launch_pddp(const PddpArgs& a, int dtype, hipStream_t s);
 
+// Kept-key lists <-> per-group key bitmaps (`rows` = H * G rows of kpad ids /
+// ceil(N/32) words).  The encoder holds one row's bitmap in LDS.
+size_t keybits_lds_bytes(int N);
+hipError_t launch_idx_to_bits(const int32_t* idx, uint32_t* bits, int rows, int N, int K, int kpad, hipStream_t s);
+hipError_t launch_bits_to_idx(const uint32_t* bits, int32_t* idx, int rows, int N, int K, int kpad, hipStream_t s);
+
 }  // namespace mcs

@@ -53,7 +53,9 @@ class LayerInputs:
 
 
 def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, device_slots=2, heads_per_pass=4,
-        record_outputs=None, log=None):
+        record_outputs=None, log=None, compact=False):
+    """compact: cache the kept-key sets as per-group key bitmaps (encoded after
+    each anchor, decoded before each reuse into one shared list buffer)."""
     import torch
 
     import sparse_attention_diffusion_amd as mcs
@@ -66,7 +68,13 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
     d = mcs.make_dims(q0, topk=kk)
     h, n, dd = q0.shape
     g = wl.groups
-    shapes = {"perm": ((h, n), torch.int32), "idx": ((h, g, d.kpad), torch.int32), "resid": ((h, n, dd), q0.dtype)}
+    if compact:
+        shapes = {"perm": ((h, n), torch.int32), "bits": ((h, g, mcs.bits_words(n)), torch.int32),
+                  "resid": ((h, n, dd), q0.dtype)}
+        idx_scratch = torch.empty((h, g, d.kpad), dtype=torch.int32, device=dev)
+    else:
+        shapes = {"perm": ((h, n), torch.int32), "idx": ((h, g, d.kpad), torch.int32),
+                  "resid": ((h, n, dd), q0.dtype)}
     be = TorchBackend(dev)
     cache = MetaCache(layers, shapes, be, offload=offload, device_slots=device_slots)
     ws = torch.empty(mcs.mcs_workspace_bytes(d, mcs.MCS_OP_ANCHOR, heads_per_pass), dtype=torch.uint8, device=dev)
@@ -90,12 +98,17 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
             elif kind == "anchor":
                 buf = cache.anchor_buffers(layer, busy_layer=layer - 1)
                 res = dict(buf, o_dense=o_dense, lse=None)
+                if compact:
+                    res["idx"] = idx_scratch
                 mcs.mcs_anchor(q, k, v, kk, ws=ws, heads_per_pass=heads_per_pass, out=res)
+                if compact:
+                    mcs.mcs_idx_to_bits(idx_scratch, n, kk, bits=buf["bits"])
                 cache.commit_anchor(layer)
                 cache.release(layer)
             else:
                 buf = cache.get(layer)
-                mcs.mcs_reuse(q, k, v, buf["perm"], buf["idx"], buf["resid"], kk, o=out)
+                idx = mcs.mcs_bits_to_idx(buf["bits"], n, kk, idx=idx_scratch) if compact else buf["idx"]
+                mcs.mcs_reuse(q, k, v, buf["perm"], idx, buf["resid"], kk, o=out)
                 cache.release(layer)
             b.record(stream)
             times[kind].append((a, b))
@@ -123,7 +136,8 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
                 if steps > warmup else float("nan"))
     return {
         "workload": wl.name, "layers": layers, "steps": steps, "warmup": warmup, "interval": interval,
-        "density": density, "topk": kk, "offload": offload, "anchors": anchors, "reuse_steps": reuses,
+        "density": density, "topk": kk, "offload": offload, "compact": compact, "anchors": anchors,
+        "reuse_steps": reuses,
         "wall_s": round(wall, 3),
         "attention_ms": round(total_attn, 1),
         "all_dense_ms_estimate": round(all_dense, 1),
@@ -147,11 +161,13 @@ def main():
     ap.add_argument("--interval", type=int, default=5)
     ap.add_argument("--density", type=float, default=0.15)
     ap.add_argument("--offload", action="store_true")
+    ap.add_argument("--compact", action="store_true", help="cache kept-key sets as per-group key bitmaps")
     ap.add_argument("--heads-per-pass", type=int, default=4)
     args = ap.parse_args()
     wl = WORKLOADS[args.workload]
     res = run(wl, args.layers, args.steps, args.warmup, args.interval, args.density, args.offload,
-              heads_per_pass=args.heads_per_pass, log=lambda m: print(m, file=sys.stderr, flush=True))
+              heads_per_pass=args.heads_per_pass, log=lambda m: print(m, file=sys.stderr, flush=True),
+              compact=args.compact)
     print(json.dumps(res), flush=True)
 
 

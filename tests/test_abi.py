@@ -113,3 +113,14 @@ def test_python_binding_raises_on_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(_abi.McsError):
         _abi.load()
+
+
+def test_key_bitmaps_reject_bad_args(lib):
+    big = _dims(n=(1 << 20) + 1, topk=1, kpad=32)
+    assert lib.mcs_idx_to_bits(ctypes.byref(big), FAKE, FAKE, None) == _abi.MCS_EUNSUPPORTED
+    assert lib.mcs_bits_to_idx(ctypes.byref(big), FAKE, FAKE, None) == _abi.MCS_EUNSUPPORTED
+    d = _dims()
+    assert lib.mcs_idx_to_bits(ctypes.byref(d), None, FAKE, None) == _abi.MCS_EINVAL
+    assert lib.mcs_bits_to_idx(ctypes.byref(d), FAKE, ctypes.c_void_p((1 << 20) + 2), None) == _abi.MCS_EINVAL
+    assert b"aligned" in lib.mcs_last_error()
+    assert lib.mcs_idx_to_bits(ctypes.byref(_dims(topk=0)), FAKE, FAKE, None) == _abi.MCS_EINVAL

@@ -1,5 +1,6 @@
 """Meta-cache on the GPU: the host round trip is the identity, and a trajectory
-with offload + prefetch produces bit-identical outputs to the all-resident one."""
+with offload + prefetch (with list or compact bitmap entries) produces
+bit-identical outputs to the all-resident one."""
 import numpy as np
 import pytest
 import torch
@@ -27,14 +28,16 @@ def test_copy_round_trip_is_bitwise():
     assert torch.equal(back, x)
 
 
-def test_offloaded_trajectory_matches_resident_bitwise():
+@pytest.mark.parametrize("compact", [False, True])
+def test_offloaded_trajectory_matches_resident_bitwise(compact):
+    print(f"trajectory offload compact={compact}", flush=True)
     wl = W.Workload("traj_small", (4, 8, 20), 2, 128, "bf16", 64, (0.2,), 11, 0.02, 0, layers=3, steps=12)
     keys = {(s, l): None for s in (2, 3, 4, 7, 11) for l in range(3)}
     rec_a, rec_b = dict(keys), dict(keys)
     ra = trajectory.run(wl, layers=3, steps=12, warmup=2, interval=3, density=0.2, offload=False,
                         record_outputs=rec_a)
     rb = trajectory.run(wl, layers=3, steps=12, warmup=2, interval=3, density=0.2, offload=True,
-                        device_slots=2, record_outputs=rec_b)
+                        device_slots=2, record_outputs=rec_b, compact=compact)
     assert rb["bytes_d2h"] > 0 and rb["bytes_h2d"] > 0
     for key in keys:
         assert torch.equal(rec_a[key], rec_b[key]), key
