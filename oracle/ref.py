@@ -336,3 +336,103 @@ def bits_to_idx(bits_rows, n, topk, kpad):
         keys = keys[:topk]
         flat_out[r, :len(keys)] = keys
     return out
+
+
+# ---------------------------------------------------------------------------
+# Matched-density selectors (block-sparsity and matched-density-oracle
+# paragraphs): vanilla block sparsity scores C-token blocks of Q and K by their
+# mean-pooled vectors and keeps whole key blocks; the oracles keep, within the
+# same budget of keys, as much true attention mass as their structure allows:
+# whole key blocks per query block, one key set per query group, one key set
+# per query.  Blocks are runs of C consecutive token ids (N a multiple of C).
+# ---------------------------------------------------------------------------
+
+def block_means(x, c):
+    """Mean of each run of c consecutive rows: (N / c, D)."""
+    x = _f64(x)
+    n, d = x.shape
+    if n % c:
+        raise ValueError("block grid needs N to be a multiple of C")
+    return x.reshape(n // c, c, d).mean(axis=1)
+
+
+def bsa_scores(q, k, c, scale):
+    """Block score of query block b and key block j: scale * mean(q_b) . mean(k_j)."""
+    return scale * (block_means(q, c) @ block_means(k, c).T)
+
+
+def _expand_blocks(blocks, c):
+    return (np.asarray(blocks, np.int64)[:, None] * c + np.arange(c)[None, :]).reshape(-1)
+
+
+def bsa_select(q, k, c, kb, scale):
+    """Vanilla block sparsity: for each query block, the kb key blocks of highest
+    mean-pooled score (ties to the lower block id), expanded to their keys in
+    ascending order: (N / c, kb * c)."""
+    s = bsa_scores(q, k, c, scale)
+    return np.stack([_expand_blocks(topk_from_mass(row, kb), c) for row in s])
+
+
+def block_mass(q, k, c, scale, lse=None):
+    """True attention mass between blocks: B[b][j] = sum over queries i of block b
+    and keys t of block j of softmax_t(z_it)."""
+    n = _f64(q).shape[0]
+    if lse is None:
+        lse = row_lse(q, k, scale)
+    m = group_mass(q, k, lse, np.arange(n), c, scale)  # (N / c, N): groups are the query blocks
+    return m.reshape(m.shape[0], n // c, c).sum(axis=2)
+
+
+def block_oracle_select(q, k, c, kb, scale, lse=None):
+    """Block oracle: per query block, the kb key blocks of largest true mass
+    (ties to the lower block id), expanded: (N / c, kb * c)."""
+    b = block_mass(q, k, c, scale, lse)
+    return np.stack([_expand_blocks(topk_from_mass(row, kb), c) for row in b])
+
+
+def private_select(q, k, topk, scale, rows=None):
+    """Per-query oracle: each query's own top-K keys by logit (equivalently by
+    softmax weight), ties to the lower key id, ascending: (rows, K)."""
+    z = logits(q, k, scale, rows)
+    return np.stack([topk_from_mass(r, topk) for r in z])
+
+
+def sparse_lse(q, k, perm, idx, group, scale, groups=None):
+    """Natural-log logsumexp of each query's logits over its group's kept keys,
+    in token order (rows of groups not computed are NaN)."""
+    q = _f64(q)
+    n = q.shape[0]
+    out = np.full(n, np.nan)
+    gcount = -(-n // group)
+    for g in (range(gcount) if groups is None else groups):
+        mem = group_members(perm, group, g)
+        z = logits(q, _f64(k)[np.asarray(idx[g], np.int64)], scale, mem)
+        m = z.max(axis=1, keepdims=True)
+        out[mem] = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
+def captured_mass(q, k, keys_of_query, scale, lse=None):
+    """Per query: the dense softmax weight that falls on its kept keys,
+    sum over kept t of exp(z_it - L_i).  keys_of_query[i] lists query i's keys."""
+    if lse is None:
+        lse = row_lse(q, k, scale)
+    z = logits(q, k, scale)
+    return np.array([np.exp(z[i, np.asarray(keys, np.int64)] - lse[i]).sum()
+                     for i, keys in enumerate(keys_of_query)])
+
+
+def keys_per_query(perm, idx, group):
+    """Expand per-group key sets to per-query key sets (token order)."""
+    n = len(perm)
+    out = [None] * n
+    for g in range(-(-n // group)):
+        for i in group_members(perm, group, g):
+            out[int(i)] = np.asarray(idx[g], np.int64)
+    return out
+
+
+def private_attention(q, k, v, keys_of_query, scale):
+    """Each query attends over its own kept keys only (renormalised softmax)."""
+    return np.stack([sparse_attention_group(q, k, v, np.array([i]), np.asarray(keys, np.int64), scale)[0]
+                     for i, keys in enumerate(keys_of_query)])
