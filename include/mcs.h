@@ -157,6 +157,33 @@ int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, co
 int mcs_idx_to_bits(const mcs_dims* d, const int32_t* idx, uint32_t* bits, hipStream_t stream);
 int mcs_bits_to_idx(const mcs_dims* d, const uint32_t* bits, int32_t* idx, hipStream_t stream);
 
+/* Gather sharing between neighbouring groups (summary page, grouping paragraph:
+ * PDDP cuts similar queries into groups, so adjacent leaves of its tree keep
+ * overlapping key sets; the gather of K/V rows by index bounds the sparse
+ * kernel).  Groups 2p and 2p+1 of each head form pair p, P = ceil(G/2) pairs.
+ *
+ * mcs_pair_plan: from kept-key lists idx [H][G][kpad] (as mcs_select writes
+ * them: K distinct keys in [0, N) per row, -1 padded), write pidx [H][G][kpad]
+ * and ncommon int32 [H][P].  Both rows of pair p become [nc keys kept by both
+ * groups (the lowest such ids, ascending) | the group's other keys, ascending],
+ * -1 padded, with nc = 128 * floor(|common| / 128) stored in ncommon[h][p]; a
+ * lone last group (odd G) keeps its list and gets nc = 0.  Every row still holds
+ * exactly its group's kept set.  pidx may equal idx (in place).  N <=
+ * MCS_PAIRS_MAX_N (MCS_EUNSUPPORTED otherwise); idx and pidx 16-byte aligned.
+ *
+ * mcs_sparse_attn_pairs: the same result as mcs_sparse_attn on pidx (up to the
+ * order of the softmax sums), with each key of a pair's common prefix gathered
+ * once for both groups.  pidx and ncommon must come from mcs_pair_plan with the
+ * same d; an ncommon entry that is not a multiple of 128 in [0, K] is treated
+ * as 0 (no sharing, still exact).  resid_add as for mcs_sparse_attn (so this
+ * is also the reuse step on a pair-planned cache).  fp32 inputs run the plain
+ * gather kernel on pidx. */
+#define MCS_PAIRS_MAX_N (1 << 19)
+int mcs_pair_plan(const mcs_dims* d, const int32_t* idx, int32_t* pidx, int32_t* ncommon, hipStream_t stream);
+int mcs_sparse_attn_pairs(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
+                          const int32_t* pidx, const int32_t* ncommon, const void* resid_add, void* o,
+                          hipStream_t stream);
+
 /* Meta-cache transfer helper (summary page, residual paragraph: inactive cache
  * entries move to host memory and the next layer is prefetched): enqueue a copy
  * of `bytes` bytes on `stream` (kind MCS_COPY_H2D / D2H / D2D; host buffers

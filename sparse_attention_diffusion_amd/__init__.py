@@ -219,6 +219,47 @@ def mcs_bits_to_idx(bits, n: int, topk: int, idx=None, kpad: int | None = None):
     return idx
 
 
+def pairs_of(n: int) -> int:
+    """Pairs of neighbouring groups per head: ceil(G / 2), G = ceil(n / 64)."""
+    return (-(-n // GROUP) + 1) // 2
+
+
+def mcs_pair_plan(idx, n: int, topk: int, pidx=None, ncommon=None):
+    """Kept-key lists [H, G, kpad] -> (pidx [H, G, kpad], ncommon int32 [H, ceil(G/2)]): both rows of
+    each pair of groups (2p, 2p+1) list their common keys first (a multiple of 128 of them)."""
+    torch = _torch()
+    lib = _abi.load()
+    h, g, kpad = idx.shape
+    _check_rows(idx, n, g)
+    d = McsDims(heads=h, n=n, head_dim=128, group=GROUP, topk=topk, kpad=kpad, dtype=MCS_BF16,
+                power_iters=POWER_ITERS, scale=1.0)
+    if pidx is None:
+        pidx = torch.empty_like(idx)
+    _check_rows(pidx, n, g, idx.shape)
+    if ncommon is None:
+        ncommon = torch.empty((h, pairs_of(n)), dtype=torch.int32, device=idx.device)
+    if ncommon.dtype != torch.int32 or tuple(ncommon.shape) != (h, pairs_of(n)):
+        raise ValueError(f"ncommon must be int32 [{h}, {pairs_of(n)}]")
+    _abi.check(lib.mcs_pair_plan(ctypes.byref(d), _ptr(idx), _ptr(pidx), _ptr(ncommon), _stream(idx.device)))
+    return pidx, ncommon
+
+
+def mcs_sparse_attn_pairs(q, k, v, perm, pidx, ncommon, topk: int, resid_add=None, o=None):
+    """Gather-sparse attention on pair-planned lists (+ optional residual): returns o [H, N, D]."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k, v, resid_add)
+    d = make_dims(q, topk=topk, kpad=pidx.shape[2])
+    h, n, _ = q.shape
+    if ncommon.dtype != torch.int32 or tuple(ncommon.shape) != (h, pairs_of(n)):
+        raise ValueError(f"ncommon must be int32 [{h}, {pairs_of(n)}]")
+    if o is None:
+        o = torch.empty_like(q)
+    _abi.check(lib.mcs_sparse_attn_pairs(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(pidx),
+                                         _ptr(ncommon), _ptr(resid_add), _ptr(o), _stream(q.device)))
+    return o
+
+
 def mcs_copy_async(dst, src, kind: int, stream=None, event=None):
     """Enqueue a byte copy of src into dst on `stream` (default: current) and record `event`."""
     torch = _torch()

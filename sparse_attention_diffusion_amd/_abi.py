@@ -15,8 +15,9 @@ ABI_VERSION = 1
 
 EXPORTED = ("mcs_abi_version", "mcs_last_error", "mcs_workspace_bytes", "mcs_group", "mcs_select",
             "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_reuse", "mcs_idx_to_bits", "mcs_bits_to_idx",
-            "mcs_copy_async")
+            "mcs_pair_plan", "mcs_sparse_attn_pairs", "mcs_copy_async")
 BITS_MAX_N = 1 << 20
+PAIRS_MAX_N = 1 << 19
 
 
 class McsDims(ctypes.Structure):
@@ -57,6 +58,8 @@ def load():
         "mcs_reuse": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
         "mcs_idx_to_bits": (ctypes.c_int, [D, P, P, St]),
         "mcs_bits_to_idx": (ctypes.c_int, [D, P, P, St]),
+        "mcs_pair_plan": (ctypes.c_int, [D, P, P, P, St]),
+        "mcs_sparse_attn_pairs": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, St]),
         "mcs_copy_async": (ctypes.c_int, [P, P, S, I32, St, P]),
     }
     for name, (res, args) in sig.items():

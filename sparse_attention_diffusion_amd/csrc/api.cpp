@@ -286,6 +286,46 @@ int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, co
   return mcs_sparse_attn(d, q, k, v, perm, idx, resid, o, stream);
 }
 
+int mcs_pair_plan(const mcs_dims* d, const int32_t* idx, int32_t* pidx, int32_t* ncommon, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(idx, 16, "idx"));
+  CHECK(check_ptr(pidx, 16, "pidx"));
+  CHECK(check_ptr(ncommon, 4, "ncommon"));
+  if (d->n > MCS_PAIRS_MAX_N) return fail(MCS_EUNSUPPORTED, "n %d above %d for pair plans", d->n, MCS_PAIRS_MAX_N);
+  hipError_t e = mcs::launch_pair_plan(idx, pidx, ncommon, d->heads, d->n, groups_of(d), d->topk, d->kpad, stream);
+  if (e != hipSuccess) return hip_fail(e, "pair plan launch");
+  return MCS_OK;
+}
+
+int mcs_sparse_attn_pairs(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
+                          const int32_t* pidx, const int32_t* ncommon, const void* resid_add, void* o,
+                          hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(pidx, 16, "pidx"));
+  CHECK(check_ptr(ncommon, 4, "ncommon"));
+  CHECK(check_ptr(o, 16, "o"));
+  if (resid_add) CHECK(check_ptr(resid_add, 16, "resid_add"));
+  mcs::AttnArgs a = attn_args(d, q, k, v);
+  a.perm = perm;
+  a.idx = pidx;
+  a.nkeys = d->topk;
+  a.rin = resid_add;
+  a.o = o;
+  const int epi = resid_add ? mcs::EPI_ADD : mcs::EPI_PLAIN;
+  // fp32 has no LDS-staged kernel to share: every row is its group's whole kept
+  // set, so the plain gather kernel gives the same attention
+  hipError_t e = d->dtype == MCS_BF16 ? mcs::launch_attention_pairs(a, ncommon, d->head_dim, epi, stream)
+                                      : mcs::launch_attention(a, d->dtype, d->head_dim, true, epi, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "paired sparse attention launch");
+  return MCS_OK;
+}
+
 int mcs_idx_to_bits(const mcs_dims* d, const int32_t* idx, uint32_t* bits, hipStream_t stream) {
   g_err.clear();
   CHECK(check_dims(d, true));

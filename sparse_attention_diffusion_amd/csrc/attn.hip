@@ -789,7 +789,10 @@ __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const
 // zeros or unused entries), then at most one more middle step and the masked
 // last step.  Step j's rows live in stage j % 2; the keys of steps alternate
 // between ka and kb the same way.
-template <int D, bool GATHER, bool PV>
+//
+// FRESH: the pass starts the softmax (its first step fixes the offsets); false
+// when steps over other keys of the same queries came before it.
+template <int D, bool GATHER, bool PV, bool FRESH = true>
 __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
                                       LDSP char* s0, LDSP char* s1) {
   const int nsteps = (x.nkeys + 31) >> 5;
@@ -798,10 +801,10 @@ __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const
   ldma<D, PV>(s0, ka, x.rk, x.rv, x.goff);
   lkeys<D, GATHER>(kb, x.ridx, 32, x.ebase);
   if (nsteps == 1) {
-    lstep<D, GATHER, PV, true, true, false>(st, x, q, s0, s1, kb, ka, 0);
+    lstep<D, GATHER, PV, FRESH, true, false>(st, x, q, s0, s1, kb, ka, 0);
     return;
   }
-  lstep<D, GATHER, PV, true, false, true>(st, x, q, s0, s1, kb, ka, 0);
+  lstep<D, GATHER, PV, FRESH, false, true>(st, x, q, s0, s1, kb, ka, 0);
   int it = 1;
   for (; it + 2 < nsteps; it += 2) {
     lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, ka, kb, it);
@@ -881,28 +884,15 @@ __device__ __forceinline__ void lfinish(const LState<D, PV>& st, const AttnArgs&
   }
 }
 
-template <int D, bool GATHER, int EPI, bool PV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_lds_kernel(AttnArgs a) {
+// Per-lane context of group g of head h: buffer descriptors of K, V and the
+// group's key list, and the LDS addresses of this lane's copy chunk and MFMA
+// operands.
+template <int D, bool GATHER>
+__device__ __forceinline__ void lctx_init(LCtx<D>& x, const AttnArgs& a, int h, int g, int lane) {
   using L = LT<D>;
-  __shared__ __attribute__((aligned(16))) char stage0[4][L::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage1[4][L::STAGE];
-  const int lane = threadIdx.x & 63, wid = wave_id();
   const int hf = lane >> 5, lm = lane & 31;
-  const int items = a.H * a.G;
-  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
-  if (blk < 0) return;
-  const int item = blk * 4 + wid;
-  if (item >= items) return;  // waves are independent: no block-level synchronisation
-  const int h = item / a.G, g = item - h * a.G;
-  const int N = a.N;
-  const size_t head_off = (size_t)h * N * L::ROWB;
-  const uint32_t head_bytes = (uint32_t)((size_t)N * L::ROWB);
-  const auto rq = make_rsrc((const char*)a.q + head_off, head_bytes);
-  LDSP char* s0 = (LDSP char*)&stage0[wid][0];
-  LDSP char* s1 = (LDSP char*)&stage1[wid][0];
-
-  LCtx<D> x;
+  const size_t head_off = (size_t)h * a.N * L::ROWB;
+  const uint32_t head_bytes = (uint32_t)((size_t)a.N * L::ROWB);
   x.rk = make_rsrc((const char*)a.k + head_off, head_bytes);
   x.rv = make_rsrc((const char*)a.v + head_off, head_bytes);
   x.ridx = GATHER ? make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad, (uint32_t)a.kpad * 4u) : make_rsrc(nullptr, 0);
@@ -928,9 +918,15 @@ void attn_lds_kernel(AttnArgs a) {
         x.vaddr[kc][sr] = L::off(e, xch) + 8 * (i16 & 1);
       }
   }
+}
 
-  int tokq[2];
-  bool qvalid[2];
+// Token ids (through perm) and validity of the lane's two query columns, and
+// the group's Q operands (kept in registers for the whole pass).
+template <int D>
+__device__ __forceinline__ void lqueries(int (&tokq)[2], bool (&qvalid)[2], u32x4 (&q)[2][LT<D>::KCH],
+                                         const AttnArgs& a, __amdgpu_buffer_rsrc_t rq, int h, int g, int lane) {
+  using L = LT<D>;
+  const int N = a.N, hf = lane >> 5, lm = lane & 31;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int slot = g * 64 + lm + 32 * nt;
@@ -941,40 +937,50 @@ void attn_lds_kernel(AttnArgs a) {
       tokq[nt] = 0;
     }
   }
-  u32x4 q[2][L::KCH];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const uint32_t qb = (uint32_t)tokq[nt] * L::ROWB + 16u * hf;
 #pragma unroll
     for (int c = 0; c < L::KCH; ++c) q[nt][c] = bload128(rq, qb + c * 32);
   }
+}
 
-  // Stages start zeroed: a padding entry's copy may leave its slot untouched,
-  // and a masked probability times a stale non-finite value would poison O.
-  for (int o = lane * 16; o < L::STAGE; o += 64 * 16) {
+// Stages start zeroed: a padding entry's copy may leave its slot untouched,
+// and a masked probability times a stale non-finite value would poison O.
+template <int D>
+__device__ __forceinline__ void lzero(LDSP char* s0, LDSP char* s1, int lane) {
+  for (int o = lane * 16; o < LT<D>::STAGE; o += 64 * 16) {
     *(LDSP u32x4*)(s0 + o) = u32x4{0, 0, 0, 0};
     *(LDSP u32x4*)(s1 + o) = u32x4{0, 0, 0, 0};
   }
-  // The copies below land in LDS through the texture path, not in order behind
-  // these stores: the stores must be done before the first copy is issued.
+  // The copies that follow land in LDS through the texture path, not in order
+  // behind these stores: the stores must be done before the first copy is issued.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
 
-  LState<D, PV> st;
+template <int D, bool PV>
+__device__ __forceinline__ void lstate_init(LState<D, PV>& st) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     st.m[nt] = 0.0f;
     st.l[nt] = 0.0f;
     if constexpr (PV) {
 #pragma unroll
-      for (int n = 0; n < L::VT; ++n) st.o[nt][n] = f32x16{};
+      for (int n = 0; n < LT<D>::VT; ++n) st.o[nt][n] = f32x16{};
     }
   }
-  if (x.nkeys > 0) lpass<D, GATHER, PV>(st, x, q, s0, s1);
+}
 
+// Normalise and store, or, if a logit far above its query's first-tile maximum
+// overflowed the fixed offset, redo the group with the online pass (direct
+// global loads over the whole key list of x.ridx).
+template <int D, bool GATHER, int EPI, bool PV>
+__device__ __forceinline__ void lend(const LState<D, PV>& st, const LCtx<D>& x, const AttnArgs& a,
+                                     __amdgpu_buffer_rsrc_t rq, int h, const int (&tokq)[2],
+                                     const bool (&qvalid)[2], int lane, LDSP char* buf) {
+  const int hf = lane >> 5, lm = lane & 31;
   const bool ok = __builtin_isfinite(st.l[0]) && __builtin_isfinite(st.l[1]);
   if (__builtin_amdgcn_ballot_w64(!ok)) {
-    // a logit far above its query's first-tile maximum overflowed the fixed
-    // offset: redo the group with the online pass (direct global loads)
     Ctx<__bf16, D, GATHER> xo;
     xo.rk = x.rk;
     xo.rv = x.rv;
@@ -988,8 +994,180 @@ void attn_lds_kernel(AttnArgs a) {
     pass_online<__bf16, D, GATHER, PV>(so, xo, rq, tokq[0], tokq[1]);
     finish<__bf16, D, EPI, PV>(so, a, h, tokq, qvalid, lm, hf);
   } else {
-    lfinish<D, EPI, PV>(st, a, h, tokq, qvalid, lane, s0);
+    lfinish<D, EPI, PV>(st, a, h, tokq, qvalid, lane, buf);
   }
+}
+
+template <int D, bool GATHER, int EPI, bool PV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_lds_kernel(AttnArgs a) {
+  using L = LT<D>;
+  __shared__ __attribute__((aligned(16))) char stage0[4][L::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[4][L::STAGE];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int items = a.H * a.G;
+  const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
+  if (blk < 0) return;
+  const int item = blk * 4 + wid;
+  if (item >= items) return;  // waves are independent: no block-level synchronisation
+  const int h = item / a.G, g = item - h * a.G;
+  const auto rq = make_rsrc((const char*)a.q + (size_t)h * a.N * L::ROWB, (uint32_t)((size_t)a.N * L::ROWB));
+  LDSP char* s0 = (LDSP char*)&stage0[wid][0];
+  LDSP char* s1 = (LDSP char*)&stage1[wid][0];
+
+  LCtx<D> x;
+  lctx_init<D, GATHER>(x, a, h, g, lane);
+  int tokq[2];
+  bool qvalid[2];
+  u32x4 q[2][L::KCH];
+  lqueries<D>(tokq, qvalid, q, a, rq, h, g, lane);
+  lzero<D>(s0, s1, lane);
+  LState<D, PV> st;
+  lstate_init<D, PV>(st);
+  if (x.nkeys > 0) lpass<D, GATHER, PV>(st, x, q, s0, s1);
+  lend<D, GATHER, EPI, PV>(st, x, a, rq, h, tokq, qvalid, lane, s0);
+}
+
+// ---------------------------------------------------------------------------
+// Gather sharing between neighbouring groups.  Groups 2p and 2p+1 of a head are
+// adjacent leaves of the PDDP tree (similar queries), and their kept-key sets
+// overlap: on the 75,600-token workload at density 0.2 about 40% of a group's
+// keys are also kept by its neighbour.  The gather of a K/V row into LDS is the
+// bound of this kernel, and the MFMA work per gathered row is fixed by C, so a
+// row that both groups keep is gathered once and consumed by both.
+//
+// The pair plan (mcs_pair_plan) reorders each group's list as [nc keys common to
+// both groups, ascending | the group's other keys, ascending], nc a multiple of
+// 128.  One block of two waves takes one pair.  Over the common prefix the waves
+// move in macro-steps of two tiles: each wave copies one 32-key tile into its own
+// stage and both waves consume both tiles (one block barrier per macro-step, so
+// each copied row feeds 128 queries).  Then each wave walks its private keys
+// alone with the ordinary two-stage pass.  Every group still attends to exactly
+// its own K keys; only the order of the softmax sums differs from the plain
+// kernel.
+// ---------------------------------------------------------------------------
+
+// The MFMA work of one tile already in LDS (no copies, no waits).
+template <int D, bool FIRST>
+__device__ __forceinline__ void lcompute(LState<D, true>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
+                                         const LDSP char* cur) {
+  // keep the two tiles of a macro-step apart: overlapping them costs registers
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 ka[LT<D>::KCH];
+  lkread<D>(ka, cur, x.kaddr);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s[2];
+  uint32_t pk[2][8];
+  lqk<D>(s, ka, q);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 vb[2][LT<D>::VT];
+  lvread<D>(vb, cur, x.vaddr);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FIRST) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = s[nt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+      st.m[nt] = pair_max(mx) * x.c + kMargin;
+    }
+  }
+  lprobs<D, true, false>(st, s, pk, x.c);
+  __builtin_amdgcn_sched_barrier(0);
+  lpv<D>(st, pk, vb);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One macro-step over the common prefix: t0 / t1 are the tiles the two waves
+// copied (wave 0's, wave 1's stage).  ISSUE: start this wave's copy of the next
+// macro-step into own_next (keys in kn) and load the keys of the one after that
+// (list entry entry_nn) into knn.
+template <int D, bool FIRST, bool ISSUE>
+__device__ __forceinline__ void lmacro(LState<D, true>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
+                                       const LDSP char* t0, const LDSP char* t1, LDSP char* own_next,
+                                       const LKeys<D>& kn, LKeys<D>& knn, int entry_nn) {
+  // Drain this wave's loads: the current tiles' copies and the keys of the next
+  // copy, all issued a macro-step ago.  A count that spares the key loads would
+  // rely on their issue order, which the compiler is free to change (it hoists
+  // key loads above earlier copies), and a copy still in flight would then be
+  // read by both waves.  The barrier makes the partner's copies visible too,
+  // and tells that both waves finished reading the stages of the macro-step
+  // before (the ones the copies below overwrite).
+  wait_vm<0>();
+  block_barrier();
+  if constexpr (ISSUE) {
+    ldma<D, true>(own_next, kn, x.rk, x.rv, x.goff);
+    lkeys<D, true>(knn, x.ridx, entry_nn, x.ebase);
+  }
+  lcompute<D, FIRST>(st, x, q, t0);
+  lcompute<D, false>(st, x, q, t1);
+  // both tiles' LDS reads are complete before this wave reaches the next barrier
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <int D, int EPI>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_pairs_kernel(AttnArgs a, const int32_t* ncommon) {
+  using L = LT<D>;
+  __shared__ __attribute__((aligned(16))) char stage0[2][L::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[2][L::STAGE];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int P = (a.G + 1) >> 1;
+  const int blk = xcd_remap(blockIdx.x, a.H * P, a.xcd_chunk);
+  if (blk < 0) return;
+  const int h = blk / P, p = blk - h * P;
+  const int g = 2 * p + wid;
+  if (g >= a.G) return;  // the last pair of an odd G has one group (and shares nothing)
+  // A count that is not a multiple of 128 within [0, K], or a lone group, falls
+  // back to no sharing: each row still lists all of its group's keys.
+  int nc = __builtin_amdgcn_readfirstlane(ncommon[(size_t)h * P + p]);
+  if (2 * p + 1 >= a.G || nc < 0 || nc > a.nkeys || (nc & 127) != 0) nc = 0;
+  const auto rq = make_rsrc((const char*)a.q + (size_t)h * a.N * L::ROWB, (uint32_t)((size_t)a.N * L::ROWB));
+  LDSP char* own0 = (LDSP char*)&stage0[wid][0];
+  LDSP char* own1 = (LDSP char*)&stage1[wid][0];
+
+  LCtx<D> x;
+  lctx_init<D, true>(x, a, h, g, lane);
+  int tokq[2];
+  bool qvalid[2];
+  u32x4 q[2][L::KCH];
+  lqueries<D>(tokq, qvalid, q, a, rq, h, g, lane);
+  lzero<D>(own0, own1, lane);
+  LState<D, true> st;
+  lstate_init<D, true>(st);
+
+  const int ns = nc >> 6;  // macro-steps (even)
+  if (ns > 0) {
+    const LDSP char* a0 = (const LDSP char*)&stage0[0][0];
+    const LDSP char* b0 = (const LDSP char*)&stage0[1][0];
+    const LDSP char* a1 = (const LDSP char*)&stage1[0][0];
+    const LDSP char* b1 = (const LDSP char*)&stage1[1][0];
+    // copy c of this wave is list entries 32*(2c + wid) .. +31, into stage c % 2
+    LKeys<D> ka, kb;
+    lkeys<D, true>(ka, x.ridx, 32 * wid, x.ebase);
+    ldma<D, true>(own0, ka, x.rk, x.rv, x.goff);
+    lkeys<D, true>(kb, x.ridx, 32 * (2 + wid), x.ebase);
+    lmacro<D, true, true>(st, x, q, a0, b0, own1, kb, ka, 32 * (4 + wid));
+    int m = 1;
+    for (; m + 2 < ns; m += 2) {
+      lmacro<D, false, true>(st, x, q, a1, b1, own0, ka, kb, 32 * (2 * (m + 2) + wid));
+      lmacro<D, false, true>(st, x, q, a0, b0, own1, kb, ka, 32 * (2 * (m + 3) + wid));
+    }
+    lmacro<D, false, false>(st, x, q, a1, b1, own0, ka, kb, 0);
+    // both waves are done with every stage before the private passes refill them
+    block_barrier();
+  }
+  const int npriv = a.nkeys - nc;
+  if (npriv > 0) {
+    LCtx<D> xp = x;
+    xp.ridx = make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad + nc, (uint32_t)(a.kpad - nc) * 4u);
+    xp.nkeys = npriv;
+    if (ns == 0)
+      lpass<D, true, true, true>(st, xp, q, own0, own1);
+    else
+      lpass<D, true, true, false>(st, xp, q, own0, own1);
+  }
+  lend<D, true, EPI, true>(st, x, a, rq, h, tokq, qvalid, lane, own0);
 }
 
 template <int D, bool GATHER, int EPI, bool PV>
@@ -998,6 +1176,22 @@ hipError_t launch_lds(const AttnArgs& a, hipStream_t s) {
   const int blocks = xcd_grid((items + 3) / 4);
   hipLaunchKernelGGL((attn_lds_kernel<D, GATHER, EPI, PV>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D, int EPI>
+hipError_t launch_pairs_d(const AttnArgs& a, const int32_t* ncommon, hipStream_t s) {
+  const int blocks = xcd_grid(a.H * ((a.G + 1) / 2));
+  hipLaunchKernelGGL((attn_pairs_kernel<D, EPI>), dim3(blocks), dim3(128), 0, s, a, ncommon);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pairs_e(const AttnArgs& a, const int32_t* ncommon, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_ADD: return launch_pairs_d<D, EPI_ADD>(a, ncommon, s);
+    case EPI_RESID: return launch_pairs_d<D, EPI_RESID>(a, ncommon, s);
+    default: return launch_pairs_d<D, EPI_PLAIN>(a, ncommon, s);
+  }
 }
 
 template <typename T, int D, bool GATHER, int EPI, bool PV>
@@ -1041,6 +1235,11 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, bool gat
     return head_dim == 128 ? launch_d<__bf16, 128>(a, gather, epi, pv, s) : launch_d<__bf16, 64>(a, gather, epi, pv, s);
   }
   return head_dim == 128 ? launch_d<float, 128>(a, gather, epi, pv, s) : launch_d<float, 64>(a, gather, epi, pv, s);
+}
+
+hipError_t launch_attention_pairs(const AttnArgs& a, const int32_t* ncommon, int head_dim, int epi,
+                                  hipStream_t s) {
+  return head_dim == 128 ? launch_pairs_e<128>(a, ncommon, epi, s) : launch_pairs_e<64>(a, ncommon, epi, s);
 }
 
 }  // namespace mcs

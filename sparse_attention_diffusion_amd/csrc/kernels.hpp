@@ -31,6 +31,17 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, bool gather, int epi, bool pv,
                             hipStream_t s);
+// bf16 gather-sparse attention over pair-planned lists: groups 2p and 2p+1 share
+// the gathers of their first ncommon[h][p] keys (see launch_pair_plan).
+hipError_t launch_attention_pairs(const AttnArgs& a, const int32_t* ncommon, int head_dim, int epi,
+                                  hipStream_t s);
+
+// Pair plan of kept-key lists: for each pair of groups (2p, 2p+1) of a head,
+// rewrite both rows as [common keys | own keys], the common prefix nc a multiple
+// of 128 (written to ncommon[h][p]); a lone last group keeps its list (nc = 0).
+size_t pair_plan_lds_bytes(int N);
+hipError_t launch_pair_plan(const int32_t* idx, int32_t* pidx, int32_t* ncommon, int H, int N, int G, int K, int kpad,
+                            hipStream_t s);
 
 // Selection pass 2 with the per-group top-K fused into its epilogue: summed
 // normalised probabilities of every key per query group (written to `mass`),

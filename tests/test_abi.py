@@ -124,3 +124,19 @@ def test_key_bitmaps_reject_bad_args(lib):
     assert lib.mcs_bits_to_idx(ctypes.byref(d), FAKE, ctypes.c_void_p((1 << 20) + 2), None) == _abi.MCS_EINVAL
     assert b"aligned" in lib.mcs_last_error()
     assert lib.mcs_idx_to_bits(ctypes.byref(_dims(topk=0)), FAKE, FAKE, None) == _abi.MCS_EINVAL
+
+
+def test_pair_entry_points_reject_bad_args(lib):
+    big = _dims(n=(1 << 19) + 1, head_dim=64, topk=1, kpad=32)
+    assert lib.mcs_pair_plan(ctypes.byref(big), FAKE, FAKE, FAKE, None) == _abi.MCS_EUNSUPPORTED
+    d = _dims()
+    assert lib.mcs_pair_plan(ctypes.byref(d), FAKE, FAKE, None, None) == _abi.MCS_EINVAL
+    assert lib.mcs_pair_plan(ctypes.byref(d), FAKE, ctypes.c_void_p((1 << 20) + 4), FAKE, None) == _abi.MCS_EINVAL
+    assert b"aligned" in lib.mcs_last_error()
+    assert lib.mcs_pair_plan(ctypes.byref(_dims(kpad=200)), FAKE, FAKE, FAKE, None) == _abi.MCS_EINVAL
+    args = [FAKE] * 6 + [None, FAKE, None]  # q k v perm pidx ncommon, resid, o, stream
+    assert lib.mcs_sparse_attn_pairs(ctypes.byref(_dims(group=32)), *args) == _abi.MCS_EUNSUPPORTED
+    assert lib.mcs_sparse_attn_pairs(ctypes.byref(_dims(topk=1001)), *args) == _abi.MCS_EINVAL
+    no_counts = [FAKE] * 5 + [None, None, FAKE, None]
+    assert lib.mcs_sparse_attn_pairs(ctypes.byref(d), *no_counts) == _abi.MCS_EINVAL
+    assert b"ncommon" in lib.mcs_last_error()
