@@ -10,7 +10,9 @@ One timed step is one pass of the whole hot path over that layer:
   reuse   = gather-sparse attention + cached residual,
   kernel  = gather-sparse attention alone on the cached indices (the metric's
             kernel-only figure; the pages time the kernel without selection and
-            grouping, MC-Sparse summary page, kernel-speed paragraph).
+            grouping, MC-Sparse summary page, kernel-speed paragraph);
+  pairs   = the pair plan and the pair-shared variant of the sparse kernel on
+            the same indices (reported under "pairs" and stage_ms, not in value).
 `value` is the gather-sparse attention throughput in useful TFLOP/s
 (4*N*K*D*H per launch over the kernel's average launch time, HIP events on the
 launch stream); `x_vs_dense` compares with this library's own dense attention on
@@ -208,6 +210,9 @@ def main():
                  resid=torch.empty_like(q), o_dense=torch.empty_like(q), lse=None)
     o_reuse = torch.empty_like(q)
     o_sparse = torch.empty_like(q)
+    o_pairs = torch.empty_like(q)
+    pidx = torch.empty_like(cache["idx"])
+    ncommon = torch.empty((h, mcs.pairs_of(n)), dtype=torch.int32, device=dev)
     o_dense = torch.empty_like(q)
     lse = torch.empty((h, n), dtype=torch.float32, device=dev)
 
@@ -230,6 +235,10 @@ def main():
                                                      o=o_reuse))
         _, ev["sparse"] = timed(lambda: mcs.mcs_sparse_attn(q, k, v, cache["perm"], cache["idx"], kk,
                                                             o=o_sparse))
+        # pair-shared gathers (reported beside the headline kernel, not in `value`)
+        _, ev["pair_plan"] = timed(lambda: mcs.mcs_pair_plan(cache["idx"], n, kk, pidx=pidx, ncommon=ncommon))
+        _, ev["sparse_pairs"] = timed(lambda: mcs.mcs_sparse_attn_pairs(q, k, v, cache["perm"], pidx, ncommon, kk,
+                                                                        o=o_pairs))
         if record is not None:
             record.append(ev)
 
@@ -286,6 +295,8 @@ def main():
                         "select_frac_mfma": round(flops_select / (ms["select"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                                   4)},
         "torch_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 3),
+        "pairs": {"shared_fraction": round(float(ncommon.double().sum().item()) / (h * (g // 2) * kk), 4),
+                  "sparse_pairs_tflops": round(flops_sparse / (ms["sparse_pairs"] / 1e3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": committed_traffic(wl.name, args.density)},
