@@ -61,7 +61,7 @@ enum mcs_status {
 
 enum mcs_dtype { MCS_F32 = 0, MCS_BF16 = 1 };
 
-enum mcs_op { MCS_OP_GROUP = 1, MCS_OP_SELECT = 2, MCS_OP_ANCHOR = 3 };
+enum mcs_op { MCS_OP_GROUP = 1, MCS_OP_SELECT = 2, MCS_OP_ANCHOR = 3, MCS_OP_BLOCK_SELECT = 4 };
 
 enum mcs_copy_kind { MCS_COPY_H2D = 1, MCS_COPY_D2H = 2, MCS_COPY_D2D = 3 };
 
@@ -83,7 +83,7 @@ int32_t mcs_abi_version(void);
 /* Message of the last failed call on this thread ("" if none). Never NULL. */
 const char* mcs_last_error(void);
 
-/* Workspace needed by op (MCS_OP_GROUP / SELECT / ANCHOR) when up to
+/* Workspace needed by op (MCS_OP_GROUP / SELECT / ANCHOR / BLOCK_SELECT) when up to
  * heads_per_pass heads of the selection mass are processed at once
  * (0 = all heads).  The selection stores one fp32 mass row of N entries per
  * group for each head of a pass, so heads_per_pass bounds the memory.  Any
@@ -156,6 +156,31 @@ int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, co
 #define MCS_BITS_MAX_N (1 << 20)
 int mcs_idx_to_bits(const mcs_dims* d, const int32_t* idx, uint32_t* bits, hipStream_t stream);
 int mcs_bits_to_idx(const mcs_dims* d, const uint32_t* bits, int32_t* idx, hipStream_t stream);
+
+/* Matched-density comparison (summary page, block-sparsity and gap
+ * paragraphs: training-free block sparsity scores tile blocks of Q and K by
+ * their mean-pooled vectors and keeps whole key blocks; the gap to the dense
+ * output is measured at equal density).
+ *
+ * mcs_block_select: vanilla block sparsity.  Blocks are runs of 64 consecutive
+ * token ids (N must be a multiple of 64: MCS_EUNSUPPORTED otherwise).  For
+ * every head and query block b, score each key block j by scale * mean(q over
+ * b) . mean(k over j) (fp32), keep the K / 64 key blocks of highest score (ties
+ * to the lower block id; K must be a multiple of 64: MCS_EINVAL), and write
+ * their keys ascending to idx[h][b] (-1 padded to kpad).  With perm = the
+ * identity (slot = token), idx is a selection for mcs_sparse_attn, so block and
+ * token-level selections run through the same gather kernel.  Needs workspace
+ * (op MCS_OP_BLOCK_SELECT: the block means); q, k 16-byte aligned.
+ *
+ * mcs_sparse_lse: the natural-log logsumexp of each query's logits
+ * scale * q_i . k_j over its group's kept keys (perm, idx as for
+ * mcs_sparse_attn), written to lse [H][N] in token order.  With the dense
+ * logsumexp L_i (mcs_dense_attn), exp(lse_i - L_i) is the share of query i's
+ * dense softmax mass that its kept keys capture. */
+int mcs_block_select(const mcs_dims* d, const void* q, const void* k, int32_t* idx, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+int mcs_sparse_lse(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const int32_t* idx, float* lse,
+                   hipStream_t stream);
 
 /* Gather sharing between neighbouring groups (summary page, grouping paragraph:
  * PDDP cuts similar queries into groups, so adjacent leaves of its tree keep

@@ -16,7 +16,7 @@ import math
 
 from . import _abi
 from ._abi import (MCS_BF16, MCS_COPY_D2D, MCS_COPY_D2H, MCS_COPY_H2D, MCS_F32, MCS_OP_ANCHOR,  # noqa: F401
-                   MCS_OP_GROUP, MCS_OP_SELECT, McsDims, McsError)
+                   MCS_OP_BLOCK_SELECT, MCS_OP_GROUP, MCS_OP_SELECT, McsDims, McsError)
 
 GROUP = 64
 POWER_ITERS = 32
@@ -167,6 +167,35 @@ def mcs_reuse(q, k, v, perm, idx, resid, topk: int, o=None):
     _abi.check(lib.mcs_reuse(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(idx), _ptr(resid),
                              _ptr(o), _stream(q.device)))
     return o
+
+
+def mcs_block_select(q, k, topk: int, ws=None, idx=None):
+    """Vanilla block sparsity (mean-pooled 64-token blocks): returns idx int32 [H, N/64, kpad] of the
+    topk/64 best-scoring key blocks per query block, expanded ascending (use with an identity perm)."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k)
+    d = make_dims(q, topk=topk)
+    h, n, _ = q.shape
+    if idx is None:
+        idx = torch.empty((h, -(-n // GROUP), d.kpad), dtype=torch.int32, device=q.device)
+    ws = _workspace(d, MCS_OP_BLOCK_SELECT, q.device, ws, 0)
+    _abi.check(lib.mcs_block_select(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(idx), _ptr(ws), ws.numel(),
+                                    _stream(q.device)))
+    return idx
+
+
+def mcs_sparse_lse(q, k, perm, idx, topk: int, lse=None):
+    """Logsumexp of each query's logits over its group's kept keys: float32 [H, N] (token order)."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k)
+    d = make_dims(q, topk=topk, kpad=idx.shape[2])
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _abi.check(lib.mcs_sparse_lse(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(perm), _ptr(idx), _ptr(lse),
+                                  _stream(q.device)))
+    return lse
 
 
 def bits_words(n: int) -> int:

@@ -9,13 +9,13 @@ LIB_PATH = os.path.join(PKG, "libmcs.so")
 
 MCS_OK, MCS_EINVAL, MCS_EUNSUPPORTED, MCS_EWORKSPACE, MCS_EHIP = 0, -1, -2, -3, -4
 MCS_F32, MCS_BF16 = 0, 1
-MCS_OP_GROUP, MCS_OP_SELECT, MCS_OP_ANCHOR = 1, 2, 3
+MCS_OP_GROUP, MCS_OP_SELECT, MCS_OP_ANCHOR, MCS_OP_BLOCK_SELECT = 1, 2, 3, 4
 MCS_COPY_H2D, MCS_COPY_D2H, MCS_COPY_D2D = 1, 2, 3
 ABI_VERSION = 1
 
 EXPORTED = ("mcs_abi_version", "mcs_last_error", "mcs_workspace_bytes", "mcs_group", "mcs_select",
             "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_reuse", "mcs_idx_to_bits", "mcs_bits_to_idx",
-            "mcs_pair_plan", "mcs_sparse_attn_pairs", "mcs_copy_async")
+            "mcs_pair_plan", "mcs_sparse_attn_pairs", "mcs_block_select", "mcs_sparse_lse", "mcs_copy_async")
 BITS_MAX_N = 1 << 20
 PAIRS_MAX_N = 1 << 19
 
@@ -59,6 +59,8 @@ def load():
         "mcs_idx_to_bits": (ctypes.c_int, [D, P, P, St]),
         "mcs_bits_to_idx": (ctypes.c_int, [D, P, P, St]),
         "mcs_pair_plan": (ctypes.c_int, [D, P, P, P, St]),
+        "mcs_block_select": (ctypes.c_int, [D, P, P, P, P, S, St]),
+        "mcs_sparse_lse": (ctypes.c_int, [D, P, P, P, P, P, St]),
         "mcs_sparse_attn_pairs": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, St]),
         "mcs_copy_async": (ctypes.c_int, [P, P, S, I32, St, P]),
     }

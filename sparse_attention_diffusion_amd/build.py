@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmcs.so")
-SOURCES = ["attn.hip", "select.hip", "pddp.hip", "keybits.hip", "pairs.hip", "api.cpp"]
+SOURCES = ["attn.hip", "select.hip", "pddp.hip", "keybits.hip", "pairs.hip", "blocksel.hip", "api.cpp"]
 # Attention keeps its 64x128 fp32 output tile in VGPRs (MFMA accumulators in the
 # VGPR form), so the rare rescale of O needs no copies between register files.
 EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/mcs.h"
+#include "blocksel.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -154,6 +155,7 @@ int mcs_workspace_bytes(const mcs_dims* d, int32_t op, int32_t hpp, size_t* byte
       *bytes = a > b ? a : b;
       return MCS_OK;
     }
+    case MCS_OP_BLOCK_SELECT: *bytes = align256(mcs::block_select_ws_bytes(d->heads, d->n, d->head_dim)); return MCS_OK;
     default: return fail(MCS_EINVAL, "unknown op %d", op);
   }
 }
@@ -323,6 +325,45 @@ int mcs_sparse_attn_pairs(const mcs_dims* d, const void* q, const void* k, const
   hipError_t e = d->dtype == MCS_BF16 ? mcs::launch_attention_pairs(a, ncommon, d->head_dim, epi, stream)
                                       : mcs::launch_attention(a, d->dtype, d->head_dim, true, epi, true, stream);
   if (e != hipSuccess) return hip_fail(e, "paired sparse attention launch");
+  return MCS_OK;
+}
+
+int mcs_block_select(const mcs_dims* d, const void* q, const void* k, int32_t* idx, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(idx, 4, "idx"));
+  CHECK(check_ptr(ws, 256, "workspace"));
+  if (d->n % 64 != 0) return fail(MCS_EUNSUPPORTED, "block selection needs n (%d) to be a multiple of 64", d->n);
+  if (d->topk % 64 != 0) return fail(MCS_EINVAL, "topk %d is not a whole number of 64-token blocks", d->topk);
+  if (!mcs::block_select_fits(d->n, d->head_dim))
+    return fail(MCS_EUNSUPPORTED, "n %d: too many blocks for one selection block", d->n);
+  const size_t need = mcs::block_select_ws_bytes(d->heads, d->n, d->head_dim);
+  if (ws_bytes < need) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipError_t e = mcs::launch_block_select(q, k, d->dtype, d->heads, d->n, d->head_dim, d->topk / 64, d->kpad,
+                                          d->scale, idx, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "block selection launch");
+  return MCS_OK;
+}
+
+int mcs_sparse_lse(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const int32_t* idx, float* lse,
+                   hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(idx, 16, "idx"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  mcs::AttnArgs a = attn_args(d, q, k, nullptr);
+  a.perm = perm;
+  a.idx = idx;
+  a.nkeys = d->topk;
+  a.lse = lse;
+  hipError_t e = mcs::launch_attention(a, d->dtype, d->head_dim, true, mcs::EPI_PLAIN, false, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse logsumexp launch");
   return MCS_OK;
 }
 

@@ -140,3 +140,20 @@ def test_pair_entry_points_reject_bad_args(lib):
     no_counts = [FAKE] * 5 + [None, None, FAKE, None]
     assert lib.mcs_sparse_attn_pairs(ctypes.byref(d), *no_counts) == _abi.MCS_EINVAL
     assert b"ncommon" in lib.mcs_last_error()
+
+
+def test_block_select_and_sparse_lse_reject_bad_args(lib):
+    d = _dims(n=1024, topk=256, kpad=256)
+    ws = ctypes.c_size_t(0)
+    assert lib.mcs_workspace_bytes(ctypes.byref(d), _abi.MCS_OP_BLOCK_SELECT, 0, ctypes.byref(ws)) == _abi.MCS_OK
+    assert ws.value >= 2 * 2 * 16 * 128 * 4
+    big = ctypes.c_size_t(1 << 30)
+    assert lib.mcs_block_select(ctypes.byref(_dims(n=1000, topk=192, kpad=192)), FAKE, FAKE, FAKE, FAKE, big,
+                                None) == _abi.MCS_EUNSUPPORTED
+    assert lib.mcs_block_select(ctypes.byref(_dims(n=1024, topk=200, kpad=224)), FAKE, FAKE, FAKE, FAKE, big,
+                                None) == _abi.MCS_EINVAL
+    assert b"block" in lib.mcs_last_error()
+    assert lib.mcs_block_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.c_size_t(16), None) \
+        == _abi.MCS_EWORKSPACE
+    assert lib.mcs_sparse_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) == _abi.MCS_EINVAL
+    assert b"lse" in lib.mcs_last_error()
