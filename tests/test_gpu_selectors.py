@@ -128,3 +128,20 @@ def test_study_harness_properties():
         assert step["residual"]["max_abs"] <= 2e-2, (name, step)
         assert step["residual"]["mean_abs"] <= 2e-3, (name, step)
         assert step["no_residual"]["mean_abs"] == pytest.approx(r["anchor_error"]["mean_abs"], rel=1e-6)
+
+
+def test_drift_study_properties():
+    # the anchor-interval study on the tiny fp32 workload: with zero drift the
+    # reuse step plus residual is dense attention and neither the residual nor
+    # the output moves; with drift both move, and the per-step cost of a gap of
+    # g steps falls towards the reuse cost as g grows
+    from sparse_attention_diffusion_amd import drift
+    still = drift.run("tiny", density=0.2, steps=2, drift=0.0, reps=1)
+    for s in still["steps"]:
+        assert s["reuse_max_abs"] <= 1e-4 and s["resid_change_rel"] <= 1e-5 and s["output_change_rel"] == 0.0
+    moving = drift.run("tiny", density=0.2, steps=3, drift=0.05, reps=1)
+    rel = [s["output_change_rel"] for s in moving["steps"]]
+    assert all(r > 0 for r in rel) and rel[-1] > rel[0]
+    assert all(s["reuse_mean_abs"] < s["no_residual_mean_abs"] for s in moving["steps"])
+    eff = [g["effective_density"] for g in moving["gap"]]
+    assert all(b < a for a, b in zip(eff, eff[1:]))
