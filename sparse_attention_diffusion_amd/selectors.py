@@ -56,9 +56,16 @@ def run(grid=(20, 45, 80), heads=8, density=0.2, steps=4, drift=0.02, seed=5, de
 
     anchor = mcs.mcs_anchor(q, k, v, kk, want_lse=True)
     o_dense, lse_dense = anchor["o_dense"], anchor["lse"]
-    sel = {"ours": (anchor["perm"], anchor["idx"]), "block": (ident, mcs.mcs_block_select(q, k, kk))}
+    idx_block = mcs.mcs_block_select(q, k, kk)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    mcs.mcs_block_select(q, k, kk, idx=idx_block)
+    b.record()
+    b.synchronize()
+    sel = {"ours": (anchor["perm"], anchor["idx"]), "block": (ident, idx_block)}
     out = {"grid": list(grid), "tokens": n, "heads": heads, "head_dim": 128, "density": kk / n, "topk": kk,
-           "drift_sigma": drift, "selectors": {}}
+           "drift_sigma": drift, "block_select_ms": round(a.elapsed_time(b), 3), "selectors": {}}
     resid = {}
     for name, (perm, idx) in sel.items():
         o_s = mcs.mcs_sparse_attn(q, k, v, perm, idx, kk)
@@ -91,6 +98,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     res = run(tuple(args.grid), args.heads, args.density, args.steps, args.drift)
     print(json.dumps(res))
+    print(f"[selectors] block selection of {res['tokens']} tokens x {res['heads']} heads: {res['block_select_ms']:.2f} ms",
+          file=sys.stderr)
     for name, r in res["selectors"].items():
         last = r["reuse"][-1] if r["reuse"] else None
         print(f"[selectors] {name:5s}: captured mass {r['captured_mass_mean']:.4f} (p10 {r['captured_mass_p10']:.4f}); "
