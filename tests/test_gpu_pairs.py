@@ -94,7 +94,8 @@ def test_plan_in_place():
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 @pytest.mark.parametrize("n,k,overlap", [(1000, 205, 0.8), (1000, 1000, 1.0), (2000, 700, 0.5), (130, 64, 1.0),
-                                         (1000, 1, 1.0), (576, 500, 0.95), (1111, 333, 0.0)])
+                                         (1000, 1, 1.0), (576, 500, 0.95), (1111, 333, 0.0),
+                                         (1000, 256, 1.0), (700, 128, 1.0), (2000, 640, 1.0)])
 def test_paired_attention_matches_oracle(dtype, d, n, k, overlap):
     print(f"paired attention {dtype} d={d} n={n} k={k} overlap={overlap}", flush=True)
     h = 2
