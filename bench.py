@@ -266,6 +266,8 @@ def main():
     levels = max(1, (g - 1).bit_length())
     pddp_bytes = levels * (2.0 * n * d * h * q.element_size() + 24.0 * n * h)
     flops_select = 4.0 * n * n * d * h
+    # K and V rows the sparse kernel gathers into LDS (mostly served by L2 / MALL)
+    gather_bytes = 2.0 * g * kk * d * q.element_size() * h
     sdpa_ms = None if args.no_sdpa else sdpa_context(q, k, v)
     out = {
         "metric": "gather-sparse attn TFLOP/s, % MFMA peak, x vs dense @ density 0.2, 75,600 tok",
@@ -289,7 +291,8 @@ def main():
         "dense_tflops": round(flops_dense / t_dense / 1e12, 2),
         "stage_ms": {key: round(val, 3) for key, val in ms.items()},
         "cache": "cold (512 MB written before every timed call)" if args.cold else "warm",
-        "stage_rates": {"group_ref_gbps": round(pddp_bytes / (ms["group"] / 1e3) / 1e9, 1),
+        "stage_rates": {"sparse_gather_tbps": round(gather_bytes / t_sparse / 1e12, 2),
+                        "group_ref_gbps": round(pddp_bytes / (ms["group"] / 1e3) / 1e9, 1),
                         "group_ref_frac_hbm": round(pddp_bytes / (ms["group"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                         "select_tflops": round(flops_select / (ms["select"] / 1e3) / 1e12, 1),
                         "select_frac_mfma": round(flops_select / (ms["select"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
