@@ -16,6 +16,10 @@
  *   q, k, v, o, resid : [H][N][D], element type d->dtype (fp32 or bf16)
  *   perm              : int32 [H][N]; perm[h][s] is the token held by slot s.
  *                       Group g of head h is slots [g*C, min((g+1)*C, N)).
+ *                       An entry outside [0, N) marks an empty slot: selection
+ *                       gives it no weight and attention writes no output for
+ *                       it (so a perm holding one token per group makes
+ *                       mcs_select a per-query top-K for those tokens).
  *   idx               : int32 [H][G][kpad], G = ceil(N/C); row (h, g) lists
  *                       the K kept key ids of group g in ascending order, then
  *                       kpad - K entries of -1.

@@ -9,7 +9,12 @@ Both selectors keep the same number of keys, K = density * N (a whole number of
   * ours:  PDDP groups of 64 similar queries, exact per-group top-K by summed
            softmax mass (the anchor step);
   * block: vanilla block sparsity, query blocks of 64 consecutive tokens scoring
-           key blocks by mean-pooled vectors (mcs_block_select).
+           key blocks by mean-pooled vectors (mcs_block_select);
+  * per-query oracle, on a sample: one query per PDDP group (its group's first
+           slot) keeps its own top K keys, by running the same exact selection
+           on a perm that holds only that query in each group (empty slots
+           carry no weight).  All three selectors are also reported on this
+           sample, for a like-for-like comparison.
 Reported per selector, over all heads and queries:
   * captured mass: the share of each query's dense softmax weight on its kept
     keys, exp(lse_sparse - lse_dense) (mcs_sparse_lse, mcs_dense_attn);
@@ -75,6 +80,21 @@ def run(grid=(20, 45, 80), heads=8, density=0.2, steps=4, drift=0.02, seed=5, de
         out["selectors"][name] = {"captured_mass_mean": round(cap.mean().item(), 5),
                                   "captured_mass_p10": round(torch.quantile(cap.flatten()[::97].float(), 0.1).item(), 5),
                                   "anchor_error": _errors(o_s, o_dense), "reuse": []}
+    # the per-query oracle on one query per group, and the other selectors on the same queries
+    sample_perm = torch.full_like(anchor["perm"], -1)
+    sample_perm[:, ::64] = anchor["perm"][:, ::64]
+    tok = anchor["perm"][:, ::64].long()
+    idx_pq = mcs.mcs_select(q, k, sample_perm, kk, lse=lse_dense)
+    sampled = {"queries_per_head": int(tok.shape[1])}
+    runs = {"per_query": (sample_perm, idx_pq), "ours": sel["ours"], "block": sel["block"]}
+    dense_rows = torch.gather(o_dense, 1, tok[..., None].expand(-1, -1, o_dense.shape[2]))
+    for name, (perm, idx) in runs.items():
+        lse_s = mcs.mcs_sparse_lse(q, k, perm, idx, kk)
+        o_s = mcs.mcs_sparse_attn(q, k, v, perm, idx, kk)
+        cap = torch.exp(torch.gather(lse_s, 1, tok) - torch.gather(lse_dense, 1, tok))
+        rows = torch.gather(o_s, 1, tok[..., None].expand(-1, -1, o_s.shape[2]))
+        sampled[name] = {"captured_mass_mean": round(cap.mean().item(), 5), "anchor_error": _errors(rows, dense_rows)}
+    out["sampled_queries"] = sampled
     for t in range(1, steps + 1):
         qt, kt, vt = W.make_qkv_torch(wl, dev, step=t)
         o_t, _ = mcs.mcs_dense_attn(qt, kt, vt)
@@ -100,6 +120,11 @@ def main(argv=None):
     print(json.dumps(res))
     print(f"[selectors] block selection of {res['tokens']} tokens x {res['heads']} heads: {res['block_select_ms']:.2f} ms",
           file=sys.stderr)
+    sq = res["sampled_queries"]
+    print(f"[selectors] one query per group ({sq['queries_per_head']} per head): captured mass per-query oracle "
+          f"{sq['per_query']['captured_mass_mean']:.4f}, ours {sq['ours']['captured_mass_mean']:.4f}, block "
+          f"{sq['block']['captured_mass_mean']:.4f}; mean-abs error {sq['per_query']['anchor_error']['mean_abs']:.3e} / "
+          f"{sq['ours']['anchor_error']['mean_abs']:.3e} / {sq['block']['anchor_error']['mean_abs']:.3e}", file=sys.stderr)
     for name, r in res["selectors"].items():
         last = r["reuse"][-1] if r["reuse"] else None
         print(f"[selectors] {name:5s}: captured mass {r['captured_mass_mean']:.4f} (p10 {r['captured_mass_p10']:.4f}); "

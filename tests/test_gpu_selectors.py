@@ -9,7 +9,7 @@ import torch
 import sparse_attention_diffusion_amd as mcs
 from oracle import ref
 from sparse_attention_diffusion_amd import workloads as W
-from tests.gpu_util import assert_close, dev, host, random_groups, to_dev
+from tests.gpu_util import assert_close, check_index_row, dev, host, random_groups, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -145,3 +145,41 @@ def test_drift_study_properties():
     assert all(s["reuse_mean_abs"] < s["no_residual_mean_abs"] for s in moving["steps"])
     eff = [g["effective_density"] for g in moving["gap"]]
     assert all(b < a for a, b in zip(eff, eff[1:]))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("n,k", [(1000, 205), (640, 64), (130, 33)])
+def test_select_on_one_query_per_group_is_per_query_topk(dtype, d, n, k):
+    # empty slots (perm entries outside [0, N)) carry no weight: a perm holding one
+    # token per group turns the group top-K into that token's own top-K, and the
+    # sparse kernels then attend for that token only
+    heads = 2
+    r = np.random.default_rng(n + 3 * k)
+    q = W.store(1.5 * r.standard_normal((heads, n, d)), dtype)
+    kk = W.store(1.5 * r.standard_normal((heads, n, d)), dtype)
+    v = W.store(r.standard_normal((heads, n, d)), dtype)
+    g = -(-n // 64)
+    toks = np.stack([r.choice(n, g, replace=False) for _ in range(heads)]).astype(np.int32)
+    perm = np.full((heads, n), -1, np.int32)
+    perm[:, ::64] = toks
+    tq, tk, tv = (to_dev(x, dtype) for x in (q, kk, v))
+    tperm = torch.from_numpy(perm).to(dev())
+    idx = mcs.mcs_select(tq, tk, tperm, k)
+    # empty slots get no output: start from zeros so every row read back is defined
+    o = mcs.mcs_sparse_attn(tq, tk, tv, tperm, idx, k, o=torch.zeros_like(tq))
+    lse = mcs.mcs_sparse_lse(tq, tk, tperm, idx, k, lse=torch.zeros(tq.shape[:2], device=dev()))
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(d)
+    mx, mn = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-5)
+    for h in range(heads):
+        lse_full = ref.row_lse(q[h], kk[h], scale)
+        idx_h = host(idx)[h]
+        for gi in range(g):
+            t = int(toks[h, gi])
+            mass = np.exp(ref.logits(q[h], kk[h], scale, np.array([t]))[0] - lse_full[t])
+            check_index_row(idx_h[gi], mass, k, n)
+        keys = [idx_h[gi][:k] for gi in range(g)]
+        want = ref.private_attention(q[h][toks[h]], kk[h], v[h], keys, scale)
+        assert_close(host(o)[h][toks[h]], want, mx, mn, f"per-query attention h{h}")
+        cap = ref.captured_mass(q[h][toks[h]], kk[h], keys, scale, lse_full[toks[h]])
+        assert_close(np.exp(host(lse)[h][toks[h]] - lse_full[toks[h]]), cap, 5e-4, 5e-5, f"per-query mass h{h}")
