@@ -14,6 +14,9 @@ Two modes:
   side stream, gated by events so that the compute stream never reads a slot
   whose copy has not finished and the side stream never overwrites a slot the
   compute stream may still read.
+Offload can keep the first `resident_layers` layers resident (the layers that fit
+a device-memory budget): those have their own buffers and are never copied, and
+only the others go through the slot pool and the host.
 
 All copies go through `mcs_copy_async` of the C ABI (or an injected copier with
 the same signature for host-only tests); streams and events are torch's
@@ -77,37 +80,42 @@ class MetaCache:
     """Per-layer cache of named device tensors (perm, idx or bits, resid) with
     optional host offload."""
 
-    def __init__(self, layers, shapes, backend, offload=False, device_slots=2):
+    def __init__(self, layers, shapes, backend, offload=False, device_slots=2, resident_layers=0):
         """shapes: {name: (shape, dtype)} of one layer's entry, e.g. {"perm": ...,
-        "idx": ..., "resid": ...}."""
+        "idx": ..., "resid": ...}.  With offload, layers 0 .. resident_layers-1
+        stay resident; the rest share `device_slots` device slots."""
+        if resident_layers < 0:
+            raise ValueError("resident_layers must be >= 0")
         self.layers = layers
         self.shapes = shapes
         self.keys = tuple(shapes)
         self.be = backend
         self.offload = offload
-        nslots = min(layers, device_slots) if offload else layers
-        if offload and nslots < 2 and layers > 1:
+        self.resident = frozenset(range(min(layers, resident_layers) if offload else layers))
+        self.own = {layer: {k: backend.empty_device(*shapes[k]) for k in self.keys} for layer in sorted(self.resident)}
+        pooled = layers - len(self.resident)
+        nslots = min(pooled, device_slots)
+        if pooled > 1 and nslots < 2:
             raise ValueError("offload needs at least two device slots")
         self.slots = [_Slot({k: backend.empty_device(*shapes[k]) for k in self.keys}) for _ in range(nslots)]
         self.entries = [_Entry() for _ in range(layers)]
-        if offload:
-            for e in self.entries:
+        for layer, e in enumerate(self.entries):
+            if layer not in self.resident:
                 e.host = {k: backend.empty_host(*shapes[k]) for k in self.keys}
         self.bytes_d2h = 0
         self.bytes_h2d = 0
 
     # -- slot management ---------------------------------------------------
     def _slot_of(self, layer):
+        """Pool slot holding `layer`'s entry, or -1 (resident layers hold none)."""
         e = self.entries[layer]
-        return e.slot if e.state == "device" else -1
+        return e.slot if e.state == "device" and layer not in self.resident else -1
 
     def _take_slot(self, layer, avoid=()):
         """A device slot for `layer`: its own if resident, else a slot not in `avoid`
         (preferring one whose owner already left); the slot's previous owner leaves
         the device.  Returns (slot, event of the previous owner's host copy or None):
         whoever overwrites the slot must wait for that copy to have read it."""
-        if not self.offload:
-            return layer, None
         own = self._slot_of(layer)
         if own >= 0:
             return own, None
@@ -131,6 +139,9 @@ class MetaCache:
     def anchor_buffers(self, layer, busy_layer=-1):
         """Device tensors the anchor of `layer` writes into (on the compute stream).
         `busy_layer` is a layer whose slot the compute stream is still using."""
+        if layer in self.resident:
+            self.entries[layer].state = "device"
+            return self.own[layer]
         avoid = () if busy_layer < 0 or self._slot_of(busy_layer) < 0 else (self._slot_of(busy_layer),)
         i, pending = self._take_slot(layer, avoid)
         s = self.slots[i]
@@ -145,7 +156,7 @@ class MetaCache:
     def commit_anchor(self, layer):
         """Call after the anchor of `layer` was enqueued: in offload mode start the
         device -> host copy of its entry on the side stream."""
-        if not self.offload:
+        if layer in self.resident:
             return
         e = self.entries[layer]
         s = self.slots[e.slot]
@@ -161,7 +172,7 @@ class MetaCache:
 
     def prefetch(self, layer, busy_layer=-1):
         """Start bringing `layer`'s entry to the device (no-op if resident)."""
-        if not self.offload:
+        if layer in self.resident:
             return
         e = self.entries[layer]
         if e.state == "device":
@@ -189,6 +200,8 @@ class MetaCache:
         e = self.entries[layer]
         if e.state == "empty":
             raise RuntimeError(f"layer {layer} has no anchor yet")
+        if layer in self.resident:
+            return self.own[layer]
         if e.state != "device":
             self.prefetch(layer)
         s = self.slots[e.slot]
@@ -198,7 +211,7 @@ class MetaCache:
 
     def release(self, layer):
         """Mark the end of the compute stream's use of `layer`'s slot."""
-        if not self.offload:
+        if layer in self.resident:
             return
         e = self.entries[layer]
         if e.state != "device":

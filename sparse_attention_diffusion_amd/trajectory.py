@@ -52,10 +52,23 @@ class LayerInputs:
         return self.state[layer]
 
 
+def entry_bytes(wl, density, compact):
+    """Bytes of one layer's cache entry: perm (int32 [H][N]), the kept keys (int32
+    lists [H][G][kpad], or bitmaps [H][G][ceil(N/32)] when compact) and the
+    residual ([H][N][D] in the workload's dtype)."""
+    h, n, d, g = wl.heads, wl.n, wl.head_dim, wl.groups
+    kpad = -(-wl.topk(density) // 32) * 32
+    keys = g * ((n + 31) // 32) if compact else g * kpad
+    return h * (4 * n + 4 * keys + n * d * (4 if wl.dtype == "f32" else 2))
+
+
 def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, device_slots=2, heads_per_pass=4,
-        record_outputs=None, log=None, compact=False):
+        record_outputs=None, log=None, compact=False, resident_layers=0):
     """compact: cache the kept-key sets as per-group key bitmaps (encoded after
-    each anchor, decoded before each reuse into one shared list buffer)."""
+    each anchor, decoded before each reuse into one shared list buffer).
+    resident_layers: with offload, the first that many layers keep their entries
+    on the device (the layers that fit a memory budget); only the rest are
+    offloaded."""
     import torch
 
     import sparse_attention_diffusion_amd as mcs
@@ -76,7 +89,8 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
         shapes = {"perm": ((h, n), torch.int32), "idx": ((h, g, d.kpad), torch.int32),
                   "resid": ((h, n, dd), q0.dtype)}
     be = TorchBackend(dev)
-    cache = MetaCache(layers, shapes, be, offload=offload, device_slots=device_slots)
+    cache = MetaCache(layers, shapes, be, offload=offload, device_slots=device_slots,
+                      resident_layers=resident_layers)
     ws = torch.empty(mcs.mcs_workspace_bytes(d, mcs.MCS_OP_ANCHOR, heads_per_pass), dtype=torch.uint8, device=dev)
     o_dense = torch.empty_like(q0)
     out = torch.empty_like(q0)
@@ -136,7 +150,8 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
                 if steps > warmup else float("nan"))
     return {
         "workload": wl.name, "layers": layers, "steps": steps, "warmup": warmup, "interval": interval,
-        "density": density, "topk": kk, "offload": offload, "compact": compact, "anchors": anchors,
+        "density": density, "topk": kk, "offload": offload, "compact": compact,
+        "resident_layers": len(cache.resident), "anchors": anchors,
         "reuse_steps": reuses,
         "wall_s": round(wall, 3),
         "attention_ms": round(total_attn, 1),
@@ -163,11 +178,16 @@ def main():
     ap.add_argument("--offload", action="store_true")
     ap.add_argument("--compact", action="store_true", help="cache kept-key sets as per-group key bitmaps")
     ap.add_argument("--heads-per-pass", type=int, default=4)
+    ap.add_argument("--resident-gb", type=float, default=0.0,
+                    help="with --offload: keep resident as many layers' entries as fit in this many GB")
     args = ap.parse_args()
     wl = WORKLOADS[args.workload]
+    resident = 0
+    if args.offload and args.resident_gb > 0:
+        resident = min(args.layers, int(args.resident_gb * 1e9 // entry_bytes(wl, args.density, args.compact)))
     res = run(wl, args.layers, args.steps, args.warmup, args.interval, args.density, args.offload,
               heads_per_pass=args.heads_per_pass, log=lambda m: print(m, file=sys.stderr, flush=True),
-              compact=args.compact)
+              compact=args.compact, resident_layers=resident)
     print(json.dumps(res), flush=True)
 
 

@@ -170,3 +170,47 @@ def test_copy_kinds():
     cache = MetaCache(3, SHAPES, be, offload=True, device_slots=2)
     replay(cache, be, 3, steps=8)
     assert set(kinds) == {MCS_COPY_D2H, MCS_COPY_H2D}
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("layers,resident,slots", [(5, 2, 2), (6, 3, 2), (4, 3, 2), (4, 4, 2), (7, 1, 3)])
+def test_mixed_residency_orders_every_access_and_copies_only_offloaded_layers(seed, layers, resident, slots):
+    be = FakeBackend(seed)
+    copied = []
+    orig = be.copy
+
+    def copy(d, s, k, st):
+        copied.append((d.name, s.name, k))
+        orig(d, s, k, st)
+
+    be.copy = copy
+    cache = MetaCache(layers, SHAPES, be, offload=True, device_slots=slots, resident_layers=resident)
+    assert cache.resident == frozenset(range(resident))
+    host_names = {b.name for e in cache.entries for b in e.host.values()}
+    assert all(not cache.entries[l].host for l in range(resident))
+    steps, warmup, interval = 12, 2, 3
+    replay(cache, be, layers, steps=steps, warmup=warmup, interval=interval)
+    anchors = sum(1 for s in range(steps) if step_kind(s, warmup, interval) == "anchor")
+    offloaded = layers - resident
+    # every device -> host copy is of an offloaded layer, once per anchor and tensor
+    assert cache.bytes_d2h == anchors * offloaded * len(SHAPES)
+    assert all((k == MCS_COPY_D2H) == (d in host_names) for d, _, k in copied)
+    if offloaded == 0:
+        assert copied == []
+
+
+def test_resident_layers_bounds():
+    be = FakeBackend(0)
+    with pytest.raises(ValueError):
+        MetaCache(3, SHAPES, be, offload=True, resident_layers=-1)
+    cache = MetaCache(3, SHAPES, be, offload=True, resident_layers=10)
+    assert cache.resident == frozenset(range(3)) and cache.slots == []
+
+
+def test_entry_bytes_of_the_trajectory_layer():
+    from sparse_attention_diffusion_amd import workloads as W
+    from sparse_attention_diffusion_amd.trajectory import entry_bytes
+    wl = W.WORKLOADS["hunyuan_trajectory"]
+    # perm 11.4 MB + lists 3.18 GB + residual 730 MB; with bitmaps 1.40 GB
+    assert entry_bytes(wl, 0.15, False) == 24 * (4 * 118800 + 4 * 1857 * 17824 + 118800 * 128 * 2)
+    assert entry_bytes(wl, 0.15, True) == 1403235936
