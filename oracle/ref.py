@@ -126,13 +126,14 @@ def pddp_verify(q, perm, group, iters=POWER_ITERS, rel_tol=1e-5):
     its projection lies within rel_tol * (max p - min p) of the cut point
     (midpoint of the two order statistics around the cut).
 
-    Returns dict(nodes, mismatched, tolerated, bad) - `bad` counts mismatches
-    outside the tolerance window; a correct grouping has bad == 0.
+    Returns dict(nodes, mismatched, tolerated, bad, ties) - `bad` counts
+    mismatches outside the tolerance window (a correct grouping has bad == 0);
+    `ties` lists the tolerated ones as (node start slot, node size, token).
     """
     q = _f64(q)
     perm = np.asarray(perm, dtype=np.int64)
     n = q.shape[0]
-    res = dict(nodes=0, mismatched=0, tolerated=0, bad=0)
+    res = dict(nodes=0, mismatched=0, tolerated=0, bad=0, ties=[])
     if sorted(perm.tolist()) != list(range(n)):
         res["bad"] = n
         return res
@@ -157,6 +158,7 @@ def pddp_verify(q, perm, group, iters=POWER_ITERS, rel_tol=1e-5):
             res["mismatched"] += 1
             if abs(p[pos[t]] - pstar) <= width:
                 res["tolerated"] += 1
+                res["ties"].append((int(s), int(m), int(t)))
             else:
                 res["bad"] += 1
     return res

@@ -136,3 +136,71 @@ def test_reuse_with_drift_is_closer_to_dense_than_plain_sparse():
     sparse1 = ref.sparse_attention(q1[0], k1[0], v1[0], a["perm"], a["idx"], wl.group, s)
     reuse1 = ref.reuse(q1[0], k1[0], v1[0], a["perm"], a["idx"], a["resid"], wl.group, s)
     assert np.abs(reuse1 - dense1).mean() < 0.5 * np.abs(sparse1 - dense1).mean()
+
+
+# ---------------------------------------------------------------------------
+# The anchor and reuse compositions against a brute force written with plain
+# Python loops (math.exp, explicit softmax matrix, per-group sums over the perm,
+# a search over every K-subset of keys), so that a mis-wired perm, lse or index
+# set inside ref.anchor / ref.reuse cannot hide behind its own formulas.
+# ---------------------------------------------------------------------------
+import itertools
+import math
+
+
+def _bf_softmax_rows(q, k, scale):
+    n = len(q)
+    rows = []
+    for i in range(n):
+        z = [scale * sum(a * b for a, b in zip(q[i], k[j])) for j in range(n)]
+        m = max(z)
+        e = [math.exp(t - m) for t in z]
+        s = sum(e)
+        rows.append(([t / s for t in e], m + math.log(s)))
+    return rows
+
+
+def _bf_attend(qi, keys, k, v, scale):
+    w = [math.exp(scale * sum(a * b for a, b in zip(qi, k[j]))) for j in keys]
+    s = sum(w)
+    return [sum(w[t] * v[j][c] for t, j in enumerate(keys)) / s for c in range(len(v[0]))]
+
+
+def _bf_anchor(q, k, v, perm, c, kk, scale):
+    n = len(q)
+    sm = _bf_softmax_rows(q, k, scale)
+    dense = [[sum(sm[i][0][j] * v[j][cc] for j in range(n)) for cc in range(len(v[0]))] for i in range(n)]
+    idx, sparse = [], [None] * n
+    for g in range(-(-n // c)):
+        mem = perm[g * c:(g + 1) * c]
+        mass = [sum(sm[i][0][j] for i in mem) for j in range(n)]
+        best = max(itertools.combinations(range(n), kk), key=lambda sub: sum(mass[j] for j in sub))
+        idx.append(list(best))
+        for i in mem:
+            sparse[i] = _bf_attend(q[i], best, k, v, scale)
+    return dict(lse=[sm[i][1] for i in range(n)], idx=idx, o_dense=dense, o_sparse=sparse,
+                resid=[[a - b for a, b in zip(dense[i], sparse[i])] for i in range(n)])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_anchor_and_reuse_match_python_brute_force(seed):
+    # N = 10, C = 4: groups of 4, 4 and a partial group of 2; K = 4 of 10 keys
+    r = np.random.default_rng(100 + seed)
+    n, d, c, kk, scale = 10, 3, 4, 4, 0.7
+    q, k, v = (r.standard_normal((n, d)) * s for s in (1.5, 1.5, 1.0))
+    a = ref.anchor(q, k, v, c, kk, scale)
+    perm = a["perm"].tolist()
+    assert perm == ref.pddp_perm(q, c).tolist()  # the grouping stage, pinned in test_oracle_pddp
+    want = _bf_anchor(q.tolist(), k.tolist(), v.tolist(), perm, c, kk, scale)
+    assert np.allclose(a["lse"], want["lse"], atol=1e-12)
+    assert [row.tolist() for row in a["idx"]] == want["idx"]
+    for name in ("o_dense", "o_sparse", "resid"):
+        assert np.allclose(a[name], np.array(want[name]), atol=1e-12), name
+    # reuse on drifted inputs: brute-force sparse attention on the cached groups and
+    # keys plus the cached residual
+    q1, k1, v1 = (x + 0.1 * r.standard_normal((n, d)) for x in (q, k, v))
+    got = ref.reuse(q1, k1, v1, a["perm"], a["idx"], a["resid"], c, scale)
+    for g, keys in enumerate(want["idx"]):
+        for i in perm[g * c:(g + 1) * c]:
+            o = _bf_attend(q1[i].tolist(), keys, k1.tolist(), v1.tolist(), scale)
+            assert np.allclose(got[i], np.array(o) + np.array(want["resid"][i]), atol=1e-12)

@@ -196,3 +196,51 @@ def test_power_direction_matches_eigh_on_a_gapped_matrix():
     top = vecs[:, -1] * np.sign(vecs[:, -1].sum())
     assert np.allclose(v, top, atol=1e-9)
     assert np.allclose(ref.principal_direction(np.zeros((5, 5))), np.full(5, 1 / np.sqrt(5)))
+
+
+# Hand-worked tie window of the node-local verifier.  One dimension, C = 2, eight
+# tokens.  With D = 1 the covariance is a positive scalar, so the direction stays
+# +1 and a node's projections are its values minus the node mean.  Sorted root
+# order: t3 (0), t6 (1), t1 (3), t5 (7.5 - e) | t2 (7.5 + e), t0 (10), t4 (14),
+# t7 (20); the cut point p* is the midpoint of t5 and t2, i.e. 7.5 before
+# centring, and the window is 1e-5 * (20 - 0) = 2e-4.  Correct perm, depth first:
+# [t3 t6 | t1 t5 | t2 t0 | t4 t7].
+def _verify_case(e, top=20.0):
+    x = np.array([10.0, 3.0, 7.5 + e, 0.0, 14.0, 7.5 - e, 1.0, top])
+    return x[:, None]
+
+
+@pytest.mark.parametrize("e,top,perm,want", [
+    # correct grouping: nothing to report
+    (5e-5, 20.0, [3, 6, 1, 5, 2, 0, 4, 7], dict(nodes=3, mismatched=0, tolerated=0, bad=0)),
+    # t5 and t2 swapped across the root cut, both e = 5e-5 from p*: inside the window
+    # (the children {t3 t6 t1 t2} and {t5 t0 t4 t7} then split correctly)
+    (5e-5, 20.0, [3, 6, 1, 2, 5, 0, 4, 7], dict(nodes=3, mismatched=2, tolerated=2, bad=0)),
+    # the same swap with e = 3e-4: outside the 2e-4 window
+    (3e-4, 20.0, [3, 6, 1, 2, 5, 0, 4, 7], dict(nodes=3, mismatched=2, tolerated=0, bad=2)),
+    # ... but inside once the node's range grows tenfold (window 2e-3): the window is
+    # relative to the node's projection range
+    (3e-4, 200.0, [3, 6, 1, 2, 5, 0, 4, 7], dict(nodes=3, mismatched=2, tolerated=2, bad=0)),
+    # t5 (e from p*) swapped with t0 (2.5 from p*): one tolerated, one bad
+    (5e-5, 20.0, [3, 6, 1, 0, 5, 2, 4, 7], dict(nodes=3, mismatched=2, tolerated=1, bad=1)),
+    # root right, left child wrong: t1 (3) and t6 (1) sit 1 from that node's cut point 2
+    (5e-5, 20.0, [3, 1, 6, 5, 2, 0, 4, 7], dict(nodes=3, mismatched=2, tolerated=0, bad=2)),
+])
+def test_verifier_tie_window_hand_worked(e, top, perm, want):
+    rep = ref.pddp_verify(_verify_case(e, top), np.array(perm), 2)
+    assert {k: rep[k] for k in want} == want, rep
+    assert len(rep["ties"]) == rep["tolerated"]
+    assert all(s == 0 and m == 8 for s, m, _ in rep["ties"])  # every tie here is at the root
+
+
+def test_verifier_reports_which_tokens_are_near_ties():
+    rep = ref.pddp_verify(_verify_case(5e-5), np.array([3, 6, 1, 0, 5, 2, 4, 7]), 2)
+    assert rep["ties"] == [(0, 8, 5)]  # t5 tolerated; t0, 2.5 from the cut, is not
+    # a near-tie at a child node (slot range 4..7): with t4 moved from 14 to
+    # 10 + 4e-5, the right child {t2 t0 t4 t7} = {7.5+e, 10, 10+4e-5, 20} cuts
+    # between t0 and t4, each 2e-5 from the midpoint, inside the window
+    # 1e-5 * (20 - 7.5 - e); t0 and t4 are swapped there
+    x = _verify_case(5e-5)
+    x[4, 0] = 10.0 + 4e-5
+    rep = ref.pddp_verify(x, np.array([3, 6, 1, 5, 2, 4, 0, 7]), 2)
+    assert rep["bad"] == 0 and sorted(rep["ties"]) == [(4, 4, 0), (4, 4, 4)], rep
