@@ -66,6 +66,65 @@ def _check_same(ref, *ts):
             raise ValueError("q, k, v (and outputs) must share device, shape and dtype")
 
 
+# The C ABI receives bare pointers and cannot know buffer sizes: every tensor is
+# checked here, before any library call, so that a wrong dtype, shape or device
+# raises ValueError instead of reading or writing past an allocation.
+
+def _check_tensor(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _groups(n):
+    return -(-n // GROUP)
+
+
+def _check_perm(perm, q):
+    _check_tensor(perm, "perm", _torch().int32, q.shape[:2], q.device)
+
+
+def _check_idx(idx, q, topk, name="idx"):
+    """int32 [H, ceil(N/64), kpad], kpad >= topk and a multiple of 32; returns kpad."""
+    torch = _torch()
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 3:
+        raise ValueError(f"{name} must be an int32 [H, G, kpad] tensor")
+    kpad = idx.shape[2]
+    if kpad < topk or kpad % 32:
+        raise ValueError(f"{name}: kpad {kpad} must be >= topk ({topk}) and a multiple of 32")
+    _check_tensor(idx, name, torch.int32, (q.shape[0], _groups(q.shape[1]), kpad), q.device)
+    return kpad
+
+
+def _check_lse(lse, q, name="lse"):
+    if lse is not None:
+        _check_tensor(lse, name, _torch().float32, q.shape[:2], q.device)
+
+
+def _check_like(t, q, name):
+    if t is not None:
+        _check_tensor(t, name, q.dtype, q.shape, q.device)
+
+
+def _check_ws(ws, device):
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+
+
+def _check_gpu(q):
+    if not q.is_cuda:
+        raise ValueError(f"tensors must be on a GPU device, got {q.device}")
+
+
 def mcs_workspace_bytes(dims: McsDims, op: int, heads_per_pass: int = 0) -> int:
     lib = _abi.load()
     out = ctypes.c_size_t(0)
@@ -78,6 +137,7 @@ def _workspace(dims, op, device, ws, heads_per_pass):
     need = mcs_workspace_bytes(dims, op, heads_per_pass)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
+    _check_ws(ws, device)
     return ws
 
 
@@ -88,8 +148,10 @@ def mcs_group(q, power_iters: int = POWER_ITERS, ws=None, perm=None):
     d = make_dims(q, power_iters=power_iters)
     if perm is None:
         perm = torch.empty(q.shape[:2], dtype=torch.int32, device=q.device)
+    _check_perm(perm, q)
+    _check_gpu(q)
     ws = _workspace(d, MCS_OP_GROUP, q.device, ws, 0)
-    _abi.check(lib.mcs_group(ctypes.byref(d), _ptr(q), _ptr(perm), _ptr(ws), ws.numel(), _stream(q.device)))
+    _abi.check(lib.mcs_group(ctypes.byref(d), _ptr(q), _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)))
     return perm
 
 
@@ -102,6 +164,10 @@ def mcs_select(q, k, perm, topk: int, lse=None, ws=None, heads_per_pass: int = 0
     g = -(-q.shape[1] // GROUP)
     if idx is None:
         idx = torch.empty((q.shape[0], g, d.kpad), dtype=torch.int32, device=q.device)
+    d.kpad = _check_idx(idx, q, topk)
+    _check_perm(perm, q)
+    _check_lse(lse, q)
+    _check_gpu(q)
     ws = _workspace(d, MCS_OP_SELECT, q.device, ws, heads_per_pass)
     _abi.check(lib.mcs_select(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(perm), _ptr(lse), _ptr(idx), _ptr(ws),
                               ws.numel(), _stream(q.device)))
@@ -116,7 +182,9 @@ def mcs_dense_attn(q, k, v, want_lse: bool = False, o=None):
     d = make_dims(q)
     if o is None:
         o = torch.empty_like(q)
+    _check_like(o, q, "o")
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if want_lse else None
+    _check_gpu(q)
     _abi.check(lib.mcs_dense_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                   _stream(q.device)))
     return o, lse
@@ -127,9 +195,12 @@ def mcs_sparse_attn(q, k, v, perm, idx, topk: int, resid_add=None, o=None):
     torch = _torch()
     lib = _abi.load()
     _check_same(q, k, v, resid_add)
-    d = make_dims(q, topk=topk, kpad=idx.shape[2])
+    d = make_dims(q, topk=topk, kpad=_check_idx(idx, q, topk))
+    _check_perm(perm, q)
     if o is None:
         o = torch.empty_like(q)
+    _check_like(o, q, "o")
+    _check_gpu(q)
     _abi.check(lib.mcs_sparse_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(idx),
                                    _ptr(resid_add), _ptr(o), _stream(q.device)))
     return o
@@ -149,6 +220,15 @@ def mcs_anchor(q, k, v, topk: int, power_iters: int = POWER_ITERS, want_lse: boo
                    idx=torch.empty((h, g, d.kpad), dtype=torch.int32, device=q.device),
                    resid=torch.empty_like(q), o_dense=torch.empty_like(q),
                    lse=torch.empty((h, n), dtype=torch.float32, device=q.device) if want_lse else None)
+    for key in ("perm", "idx", "resid", "o_dense"):
+        if out.get(key) is None:
+            raise ValueError(f"out[{key!r}] is required")
+    _check_perm(out["perm"], q)
+    d.kpad = _check_idx(out["idx"], q, topk, "out['idx']")
+    _check_like(out["resid"], q, "out['resid']")
+    _check_like(out["o_dense"], q, "out['o_dense']")
+    _check_lse(out.get("lse"), q, "out['lse']")
+    _check_gpu(q)
     ws = _workspace(d, MCS_OP_ANCHOR, q.device, ws, heads_per_pass)
     _abi.check(lib.mcs_anchor(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(out["perm"]), _ptr(out["idx"]),
                               _ptr(out["resid"]), _ptr(out["o_dense"]), _ptr(out.get("lse")), _ptr(ws),
@@ -161,9 +241,14 @@ def mcs_reuse(q, k, v, perm, idx, resid, topk: int, o=None):
     torch = _torch()
     lib = _abi.load()
     _check_same(q, k, v, resid)
-    d = make_dims(q, topk=topk, kpad=idx.shape[2])
+    if resid is None:
+        raise ValueError("resid is required")
+    d = make_dims(q, topk=topk, kpad=_check_idx(idx, q, topk))
+    _check_perm(perm, q)
     if o is None:
         o = torch.empty_like(q)
+    _check_like(o, q, "o")
+    _check_gpu(q)
     _abi.check(lib.mcs_reuse(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(idx), _ptr(resid),
                              _ptr(o), _stream(q.device)))
     return o
@@ -179,8 +264,10 @@ def mcs_block_select(q, k, topk: int, ws=None, idx=None):
     h, n, _ = q.shape
     if idx is None:
         idx = torch.empty((h, -(-n // GROUP), d.kpad), dtype=torch.int32, device=q.device)
+    d.kpad = _check_idx(idx, q, topk)
+    _check_gpu(q)
     ws = _workspace(d, MCS_OP_BLOCK_SELECT, q.device, ws, 0)
-    _abi.check(lib.mcs_block_select(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(idx), _ptr(ws), ws.numel(),
+    _abi.check(lib.mcs_block_select(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(idx), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(q.device)))
     return idx
 
@@ -190,9 +277,12 @@ def mcs_sparse_lse(q, k, perm, idx, topk: int, lse=None):
     torch = _torch()
     lib = _abi.load()
     _check_same(q, k)
-    d = make_dims(q, topk=topk, kpad=idx.shape[2])
+    d = make_dims(q, topk=topk, kpad=_check_idx(idx, q, topk))
+    _check_perm(perm, q)
     if lse is None:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _check_lse(lse, q)
+    _check_gpu(q)
     _abi.check(lib.mcs_sparse_lse(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(perm), _ptr(idx), _ptr(lse),
                                   _stream(q.device)))
     return lse
@@ -203,28 +293,39 @@ def bits_words(n: int) -> int:
     return (n + 31) // 32
 
 
-def _check_rows(t, n, g, shape=None):
+def _check_rows(t, n, g, shape=None, device=None):
     """One row per (head, group): g must be ceil(n / 64); int32 storage."""
     torch = _torch()
-    if t.dtype != torch.int32 or t.dim() != 3:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 3:
         raise ValueError("key lists and bitmaps are int32 [H, G, width]")
     if g != -(-n // GROUP):
         raise ValueError(f"{g} groups do not match n={n} (expected {-(-n // GROUP)})")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"shape {tuple(t.shape)} differs from {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"tensor on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError("key lists and bitmaps must be contiguous")
+
+
+def _check_list_width(kpad, topk):
+    if kpad < topk or kpad % 32:
+        raise ValueError(f"kpad {kpad} must be >= topk ({topk}) and a multiple of 32")
 
 
 def mcs_idx_to_bits(idx, n: int, topk: int, bits=None):
     """Kept-key lists int32 [H, G, kpad] -> key bitmaps uint32 (stored as int32) [H, G, ceil(n/32)]."""
     torch = _torch()
     lib = _abi.load()
+    _check_rows(idx, n, idx.shape[1] if idx.dim() == 3 else -1)
     h, g, kpad = idx.shape
-    _check_rows(idx, n, g)
+    _check_list_width(kpad, topk)
     d = McsDims(heads=h, n=n, head_dim=128, group=GROUP, topk=topk, kpad=kpad, dtype=MCS_BF16,
                 power_iters=POWER_ITERS, scale=1.0)
     if bits is None:
         bits = torch.empty((h, g, bits_words(n)), dtype=torch.int32, device=idx.device)
-    _check_rows(bits, n, g, (h, g, bits_words(n)))
+    _check_rows(bits, n, g, (h, g, bits_words(n)), idx.device)
+    _check_gpu(idx)
     _abi.check(lib.mcs_idx_to_bits(ctypes.byref(d), _ptr(idx), _ptr(bits), _stream(idx.device)))
     return bits
 
@@ -233,17 +334,21 @@ def mcs_bits_to_idx(bits, n: int, topk: int, idx=None, kpad: int | None = None):
     """Key bitmaps [H, G, ceil(n/32)] -> kept-key lists int32 [H, G, kpad] (ascending, -1 padded)."""
     torch = _torch()
     lib = _abi.load()
+    _check_rows(bits, n, bits.shape[1] if bits.dim() == 3 else -1)
     h, g, _ = bits.shape
     _check_rows(bits, n, g, (h, g, bits_words(n)))
     if idx is not None:
+        _check_rows(idx, n, idx.shape[1] if idx.dim() == 3 else -1)
         kpad = idx.shape[2]
     elif kpad is None:
         kpad = kpad_for(topk)
+    _check_list_width(kpad, topk)
     d = McsDims(heads=h, n=n, head_dim=128, group=GROUP, topk=topk, kpad=kpad, dtype=MCS_BF16,
                 power_iters=POWER_ITERS, scale=1.0)
     if idx is None:
         idx = torch.empty((h, g, kpad), dtype=torch.int32, device=bits.device)
-    _check_rows(idx, n, g, (h, g, kpad))
+    _check_rows(idx, n, g, (h, g, kpad), bits.device)
+    _check_gpu(bits)
     _abi.check(lib.mcs_bits_to_idx(ctypes.byref(d), _ptr(bits), _ptr(idx), _stream(bits.device)))
     return idx
 
@@ -258,17 +363,18 @@ def mcs_pair_plan(idx, n: int, topk: int, pidx=None, ncommon=None):
     each pair of groups (2p, 2p+1) list their common keys first (a multiple of 128 of them)."""
     torch = _torch()
     lib = _abi.load()
+    _check_rows(idx, n, idx.shape[1] if idx.dim() == 3 else -1)
     h, g, kpad = idx.shape
-    _check_rows(idx, n, g)
+    _check_list_width(kpad, topk)
     d = McsDims(heads=h, n=n, head_dim=128, group=GROUP, topk=topk, kpad=kpad, dtype=MCS_BF16,
                 power_iters=POWER_ITERS, scale=1.0)
     if pidx is None:
         pidx = torch.empty_like(idx)
-    _check_rows(pidx, n, g, idx.shape)
+    _check_rows(pidx, n, g, idx.shape, idx.device)
     if ncommon is None:
         ncommon = torch.empty((h, pairs_of(n)), dtype=torch.int32, device=idx.device)
-    if ncommon.dtype != torch.int32 or tuple(ncommon.shape) != (h, pairs_of(n)):
-        raise ValueError(f"ncommon must be int32 [{h}, {pairs_of(n)}]")
+    _check_tensor(ncommon, "ncommon", torch.int32, (h, pairs_of(n)), idx.device)
+    _check_gpu(idx)
     _abi.check(lib.mcs_pair_plan(ctypes.byref(d), _ptr(idx), _ptr(pidx), _ptr(ncommon), _stream(idx.device)))
     return pidx, ncommon
 
@@ -278,12 +384,14 @@ def mcs_sparse_attn_pairs(q, k, v, perm, pidx, ncommon, topk: int, resid_add=Non
     torch = _torch()
     lib = _abi.load()
     _check_same(q, k, v, resid_add)
-    d = make_dims(q, topk=topk, kpad=pidx.shape[2])
+    d = make_dims(q, topk=topk, kpad=_check_idx(pidx, q, topk, "pidx"))
     h, n, _ = q.shape
-    if ncommon.dtype != torch.int32 or tuple(ncommon.shape) != (h, pairs_of(n)):
-        raise ValueError(f"ncommon must be int32 [{h}, {pairs_of(n)}]")
+    _check_perm(perm, q)
+    _check_tensor(ncommon, "ncommon", torch.int32, (h, pairs_of(n)), q.device)
     if o is None:
         o = torch.empty_like(q)
+    _check_like(o, q, "o")
+    _check_gpu(q)
     _abi.check(lib.mcs_sparse_attn_pairs(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(pidx),
                                          _ptr(ncommon), _ptr(resid_add), _ptr(o), _stream(q.device)))
     return o
@@ -296,6 +404,13 @@ def mcs_copy_async(dst, src, kind: int, stream=None, event=None):
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("dst and src sizes differ")
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("copies need contiguous tensors")
+    want = {MCS_COPY_H2D: (False, True), MCS_COPY_D2H: (True, False), MCS_COPY_D2D: (True, True)}
+    if kind not in want:
+        raise ValueError(f"unknown copy kind {kind}")
+    if (src.is_cuda, dst.is_cuda) != want[kind]:
+        raise ValueError(f"copy kind {kind} does not match src on {src.device} and dst on {dst.device}")
     dev = src.device if src.is_cuda else dst.device
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     ev = ctypes.c_void_p(event.cuda_event) if event is not None else None

@@ -76,7 +76,7 @@ size_t select_ws(const mcs_dims* d, int hpp) { return stats_bytes(d) + (size_t)h
 
 mcs::AttnArgs attn_args(const mcs_dims* d, const void* q, const void* k, const void* v) {
   mcs::AttnArgs a{};
-  a.xcd_chunk = mcs::default_xcd_chunk();
+  a.xcd_chunk = mcs::kXcdChunk;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -108,7 +108,7 @@ int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
     m.N = d->n;
     m.G = G;
     m.c = (float)((double)d->scale * 1.4426950408889634);
-    m.xcd_chunk = mcs::default_xcd_chunk();
+    m.xcd_chunk = mcs::kXcdChunk;
     m.idx = idx;
     m.K = d->topk;
     m.kpad = d->kpad;
@@ -126,14 +126,6 @@ int heads_per_pass(const mcs_dims* d, size_t ws_bytes) {
 }
 
 }  // namespace
-
-namespace mcs {
-int default_xcd_chunk() {
-  const char* e = getenv("MCS_XCD_CHUNK");
-  if (e && *e) return atoi(e);
-  return 32;
-}
-}  // namespace mcs
 
 extern "C" {
 

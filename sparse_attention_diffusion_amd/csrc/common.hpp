@@ -103,9 +103,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 // partial window keeps the identity mapping.  Returns -1 for padding blocks.
 __device__ __forceinline__ int xcd_remap(int hw_block, int n_logical, int chunk) {
   if (hw_block >= n_logical) return -1;
+  if (chunk <= 0) return hw_block;
   const int window = kNumXcd * chunk;
   const int full = (n_logical / window) * window;
-  if (chunk <= 0 || hw_block >= full) return hw_block;
+  if (hw_block >= full) return hw_block;
   const int x = hw_block % kNumXcd, j = hw_block / kNumXcd;
   return (j / chunk) * window + x * chunk + (j % chunk);
 }

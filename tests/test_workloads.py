@@ -50,3 +50,15 @@ def test_feature_statistics():
     assert q.shape == (1, 1024, 64) and q.dtype == np.float32
     # unit-variance features plus 0.5^2 noise
     assert abs(q.var() - 1.25) < 0.1 and abs(v.var() - 1.0) < 0.05
+
+
+def test_pct_of_ideal_reproduces_the_pages_kernel_speed_figure():
+    # summary page, kernel-speed paragraph: 4.79x at density 0.2 is 96% of the
+    # ideal 1/density speedup; bench.py reports its own ratio the same way
+    import bench
+    with open(os.path.join(GOLDEN, "workload_figures.json")) as f:
+        fig = json.load(f)["kernel_speed"]
+    got = bench.pct_of_ideal(fig["speedup_vs_fa3"], fig["density"])
+    assert abs(got - 0.958) < 1e-12
+    assert round(got, 2) == fig["fraction_of_ideal"]
+    assert W.WORKLOADS["wan14b_720p"].n == fig["tokens"]
