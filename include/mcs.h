@@ -135,6 +135,17 @@ int mcs_sparse_attn(const mcs_dims* d, const void* q, const void* k, const void*
 int mcs_anchor(const mcs_dims* d, const void* q, const void* k, const void* v, int32_t* perm, int32_t* idx,
                void* resid, void* o_dense, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Residual of a supplied selection (summary page, residual paragraph: the
+ * residual is the dense output minus the sparse output on the same step):
+ * resid = o_dense - gather-sparse attention of q/k/v with perm and idx as for
+ * mcs_sparse_attn, formed in fp32 and rounded once to d->dtype.  o_dense is the
+ * dense output of the same q/k/v (mcs_dense_attn), read-only; resid may not
+ * alias it.  mcs_anchor forms its residual the same way with its own perm and
+ * idx; this entry point serves selections made elsewhere (for example block
+ * selections, mcs_block_select with an identity perm). */
+int mcs_residual(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
+                 const int32_t* idx, const void* o_dense, void* resid, hipStream_t stream);
+
 /* Reuse step (summary page, selection and residual paragraphs): o = sparse
  * attention of the current q/k/v with the cached perm and idx, plus the cached
  * resid.  No regrouping, no reselection. */

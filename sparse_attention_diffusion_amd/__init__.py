@@ -236,6 +236,26 @@ def mcs_anchor(q, k, v, topk: int, power_iters: int = POWER_ITERS, want_lse: boo
     return out
 
 
+def mcs_residual(q, k, v, perm, idx, topk: int, o_dense, resid=None):
+    """Residual of a supplied selection: o_dense - sparse attention(perm, idx), [H, N, D]."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k, v, o_dense)
+    if o_dense is None:
+        raise ValueError("o_dense is required")
+    d = make_dims(q, topk=topk, kpad=_check_idx(idx, q, topk))
+    _check_perm(perm, q)
+    if resid is None:
+        resid = torch.empty_like(q)
+    _check_like(resid, q, "resid")
+    if resid.data_ptr() == o_dense.data_ptr():
+        raise ValueError("resid may not alias o_dense")
+    _check_gpu(q)
+    _abi.check(lib.mcs_residual(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(idx), _ptr(o_dense),
+                                _ptr(resid), _stream(q.device)))
+    return resid
+
+
 def mcs_reuse(q, k, v, perm, idx, resid, topk: int, o=None):
     """Reuse step: sparse attention with cached perm/idx plus the cached residual."""
     torch = _torch()

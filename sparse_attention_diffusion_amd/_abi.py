@@ -14,7 +14,7 @@ MCS_COPY_H2D, MCS_COPY_D2H, MCS_COPY_D2D = 1, 2, 3
 ABI_VERSION = 1
 
 EXPORTED = ("mcs_abi_version", "mcs_last_error", "mcs_workspace_bytes", "mcs_group", "mcs_select",
-            "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_reuse", "mcs_idx_to_bits", "mcs_bits_to_idx",
+            "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_residual", "mcs_reuse", "mcs_idx_to_bits", "mcs_bits_to_idx",
             "mcs_pair_plan", "mcs_sparse_attn_pairs", "mcs_block_select", "mcs_sparse_lse", "mcs_copy_async")
 BITS_MAX_N = 1 << 20
 PAIRS_MAX_N = 1 << 19
@@ -55,6 +55,7 @@ def load():
         "mcs_dense_attn": (ctypes.c_int, [D, P, P, P, P, P, St]),
         "mcs_sparse_attn": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
         "mcs_anchor": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, S, St]),
+        "mcs_residual": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
         "mcs_reuse": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
         "mcs_idx_to_bits": (ctypes.c_int, [D, P, P, St]),
         "mcs_bits_to_idx": (ctypes.c_int, [D, P, P, St]),

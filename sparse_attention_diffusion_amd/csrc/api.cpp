@@ -273,6 +273,29 @@ int mcs_anchor(const mcs_dims* d, const void* q, const void* k, const void* v, i
   return MCS_OK;
 }
 
+int mcs_residual(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
+                 const int32_t* idx, const void* o_dense, void* resid, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(idx, 16, "idx"));
+  CHECK(check_ptr(o_dense, 16, "o_dense"));
+  CHECK(check_ptr(resid, 16, "resid"));
+  if (resid == o_dense) return fail(MCS_EINVAL, "resid may not alias o_dense");
+  mcs::AttnArgs sa = attn_args(d, q, k, v);
+  sa.perm = perm;
+  sa.idx = idx;
+  sa.nkeys = d->topk;
+  sa.rin = o_dense;
+  sa.o = resid;
+  hipError_t e = mcs::launch_attention(sa, d->dtype, d->head_dim, true, mcs::EPI_RESID, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "residual launch");
+  return MCS_OK;
+}
+
 int mcs_reuse(const mcs_dims* d, const void* q, const void* k, const void* v, const int32_t* perm,
               const int32_t* idx, const void* resid, void* o, hipStream_t stream) {
   g_err.clear();

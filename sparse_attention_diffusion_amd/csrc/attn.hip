@@ -138,8 +138,46 @@ struct State {
   using TL = Tile<T, D>;
   f32x16 o[2][TL::VEC];
   float m[2];   // running offset, log2 units (scaled max), per query column
-  float l[2];   // running sum of exp2(s*c - m)
+  float l[2];   // running sum of exp2(s*c - m) that normalises O
+  float lx[2];  // exact fp32 sum of the unrounded probabilities, kept for the row
+                // statistics when l sums the bf16-rounded ones (see row_sums)
 };
+
+// Row sums of one step's probabilities.  O is normalised by the sum of exactly
+// the values the PV product multiplies: for bf16 those are the probabilities
+// rounded to bf16, summed with v_dot2_f32_bf16 against ones, so a row whose
+// mass sits on one key returns that key's V row without a 2^-9 scale error.  The
+// row statistics (logsumexp, the offset and 1/sum that selection pass 2 reads)
+// need the exact fp32 sum of the unrounded values: with STATS both are kept,
+// the exact one in lx.  Without PV there is only the exact sum, in l.
+template <bool PV, bool F32, bool STATS>
+__device__ __forceinline__ void row_sums(float& l, float& lx, const f32x16& p, const uint32_t (&pk)[8]) {
+  constexpr bool PACKED = PV && !F32;
+  constexpr bool EXACT = !PACKED || STATS;
+  if constexpr (PACKED) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls = l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), one, ls, false);
+    l = ls;
+  }
+  if constexpr (EXACT) {
+    float ls = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ls += p[r];
+    if constexpr (PACKED)
+      lx += ls;
+    else
+      l += ls;
+  }
+}
+
+// The sum the row statistics are taken from (see row_sums).
+template <bool PV, bool F32, bool STATS>
+__device__ __forceinline__ float stat_sum(float l, float lx) {
+  return (PV && !F32 && STATS) ? lx : l;
+}
 
 // S^T of one 32-key step (rows: the step's keys, columns: the group's 64 queries).
 template <typename T, int D>
@@ -172,7 +210,7 @@ __device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int t0, int nkeys, int
 
 // Probabilities exp2(s*c - m) with the offsets m fixed, their bf16 packing for the
 // PV product, and the row sums.
-template <typename T, int D, bool PV, bool EXACT_SUM>
+template <typename T, int D, bool PV, bool STATS>
 __device__ __forceinline__ void probs(State<T, D, PV>& st, f32x16 (&s)[2], uint32_t (&pk)[2][8], float c) {
   using TL = Tile<T, D>;
 #pragma unroll
@@ -184,25 +222,13 @@ __device__ __forceinline__ void probs(State<T, D, PV>& st, f32x16 (&s)[2], uint3
 #pragma unroll
       for (int i = 0; i < 8; ++i) pk[nt][i] = pack_bf16x2(s[nt][2 * i], s[nt][2 * i + 1]);
     }
-    if constexpr (EXACT_SUM || TL::F32) {
-      float ls = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ls += s[nt][r];
-      st.l[nt] += ls;
-    } else {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-      float ls = st.l[nt];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[nt][i]), one, ls, false);
-      st.l[nt] = ls;
-    }
+    row_sums<PV, TL::F32, STATS>(st.l[nt], st.lx[nt], s[nt], pk[nt]);
   }
 }
 
 // Masking of entries past the key count and the online softmax update; leaves
 // the step's probabilities exp2(s*c - m) in s.
-template <typename T, int D, bool PV, bool EXACT_SUM, bool MASK>
+template <typename T, int D, bool PV, bool STATS, bool MASK>
 __device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], uint32_t (&pk)[2][8], int t0, int nkeys,
                                         float c, int hf) {
   using TL = Tile<T, D>;
@@ -226,6 +252,7 @@ __device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], uin
       const float mnew = need ? mx : st.m[nt];
       const float alpha = need ? fast_exp2(st.m[nt] - mnew) : 1.0f;
       st.l[nt] *= alpha;
+      st.lx[nt] *= alpha;
       st.m[nt] = mnew;
       if constexpr (PV) {
 #pragma unroll
@@ -243,22 +270,7 @@ __device__ __forceinline__ void softmax(State<T, D, PV>& st, f32x16 (&s)[2], uin
 #pragma unroll
       for (int i = 0; i < 8; ++i) pk[nt][i] = pack_bf16x2(s[nt][2 * i], s[nt][2 * i + 1]);
     }
-    if constexpr (EXACT_SUM || TL::F32) {
-      // fp32 row sums: the row statistics / logsumexp are consumed by selection
-      float ls = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ls += s[nt][r];
-      st.l[nt] += ls;
-    } else {
-      // sum of the bf16-rounded probabilities that the PV product uses, so the
-      // normalisation matches the numerator (v_dot2_f32_bf16 against ones)
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-      float ls = st.l[nt];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[nt][i]), one, ls, false);
-      st.l[nt] = ls;
-    }
+    row_sums<PV, TL::F32, STATS>(st.l[nt], st.lx[nt], s[nt], pk[nt]);
   }
 }
 
@@ -325,7 +337,7 @@ __device__ __forceinline__ void fixed_step(State<T, D, PV>& st, const Ctx<T, D, 
   // ilater receives those of step it+2.  The index loads are issued first so
   // that waiting for them never waits for this step's K/V gathers (the vector
   // memory counter retires in order).
-  constexpr bool EXACT = !GATHER;
+  constexpr bool STATS = !GATHER;
   load_idx<GATHER>(ilater, x.ridx, (it + 2) * 32, x.lm, x.hf);
   f32x16 s[2];
   uint32_t pk[2][8];
@@ -335,7 +347,7 @@ __device__ __forceinline__ void fixed_step(State<T, D, PV>& st, const Ctx<T, D, 
   // keep the gathers where they are: sinking them toward the end of the step
   // (which the scheduler does to shorten live ranges) exposes their latency
   __builtin_amdgcn_sched_barrier(0);
-  probs<T, D, PV, EXACT>(st, s, pk, x.c);
+  probs<T, D, PV, STATS>(st, s, pk, x.c);
   if constexpr (PV) {
     pv<T, D, PV>(st, s, pk, b);
     load_v<T, D>(b, inext, x.rv, x.lm);
@@ -345,7 +357,7 @@ __device__ __forceinline__ void fixed_step(State<T, D, PV>& st, const Ctx<T, D, 
 template <typename T, int D, bool GATHER, bool PV>
 __device__ __forceinline__ void pass_fixed(State<T, D, PV>& st, const Ctx<T, D, GATHER>& x,
                                            const u32x4 (&q)[2][Tile<T, D>::KCH]) {
-  constexpr bool EXACT = !GATHER;
+  constexpr bool STATS = !GATHER;
   Idx ia, ib;
   KV<T, D> b;
   const int nsteps = (x.nkeys + 31) >> 5;
@@ -367,7 +379,7 @@ __device__ __forceinline__ void pass_fixed(State<T, D, PV>& st, const Ctx<T, D, 
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
       st.m[nt] = pair_max(mx) * x.c + kMargin;
     }
-    probs<T, D, PV, EXACT>(st, s, pk, x.c);
+    probs<T, D, PV, STATS>(st, s, pk, x.c);
     if constexpr (PV) {
       pv<T, D, PV>(st, s, pk, b);
       if (nsteps > 1) load_v<T, D>(b, ia, x.rv, x.lm);
@@ -388,7 +400,7 @@ __device__ __forceinline__ void pass_fixed(State<T, D, PV>& st, const Ctx<T, D, 
     uint32_t pk[2][8];
     qk<T, D>(s, b, q);
     mask_tail<0>(s, (nsteps - 1) * 32, x.nkeys, x.hf);
-    probs<T, D, PV, EXACT>(st, s, pk, x.c);
+    probs<T, D, PV, STATS>(st, s, pk, x.c);
     if constexpr (PV) pv<T, D, PV>(st, s, pk, b);
   }
 }
@@ -410,12 +422,11 @@ __device__ __forceinline__ void load_q(__amdgpu_buffer_rsrc_t rq, const int (&to
 // Online pass with a running maximum and lazy rescaling (the offset moves only
 // when the maximum grows by more than 2^8).  Used only for groups whose
 // fixed-offset pass overflowed.
-template <typename T, int D, bool GATHER, bool PV>
+template <typename T, int D, bool GATHER, bool PV, bool STATS>
 __device__ __attribute__((noinline)) void pass_online(State<T, D, PV>& st, const Ctx<T, D, GATHER>& x,
                                                       __amdgpu_buffer_rsrc_t rq, int tok0, int tok1) {
   // Q is reloaded here rather than passed in: an array argument of a
   // non-inlined call would force the caller's copy into scratch memory.
-  constexpr bool EXACT = !GATHER;
   const int tokq[2] = {tok0, tok1};
   u32x4 q[2][Tile<T, D>::KCH];
   load_q<T, D>(rq, tokq, x.hf, q);
@@ -430,9 +441,9 @@ __device__ __attribute__((noinline)) void pass_online(State<T, D, PV>& st, const
     uint32_t pk[2][8];
     qk<T, D>(s, b, q);
     if (it + 1 == nsteps)
-      softmax<T, D, PV, EXACT, true>(st, s, pk, it * 32, x.nkeys, x.c, x.hf);
+      softmax<T, D, PV, STATS, true>(st, s, pk, it * 32, x.nkeys, x.c, x.hf);
     else
-      softmax<T, D, PV, EXACT, false>(st, s, pk, it * 32, x.nkeys, x.c, x.hf);
+      softmax<T, D, PV, STATS, false>(st, s, pk, it * 32, x.nkeys, x.c, x.hf);
     if constexpr (PV) pv<T, D, PV>(st, s, pk, b);
   }
 }
@@ -443,6 +454,7 @@ __device__ __forceinline__ void state_init(State<T, D, PV>& st) {
   for (int nt = 0; nt < 2; ++nt) {
     st.m[nt] = -INFINITY;
     st.l[nt] = 0.0f;
+    st.lx[nt] = 0.0f;
     if constexpr (PV) {
 #pragma unroll
       for (int cc = 0; cc < Tile<T, D>::VEC; ++cc) st.o[nt][cc] = f32x16{};
@@ -451,7 +463,7 @@ __device__ __forceinline__ void state_init(State<T, D, PV>& st) {
 }
 
 // Row statistics, normalisation and the epilogue stores of one group.
-template <typename T, int D, int EPI, bool PV>
+template <typename T, int D, int EPI, bool PV, bool STATS>
 __device__ __forceinline__ void finish(const State<T, D, PV>& st, const AttnArgs& a, int h, const int (&tokq)[2],
                                        const bool (&qvalid)[2], int lm, int hf) {
   using TL = Tile<T, D>;
@@ -460,11 +472,12 @@ __device__ __forceinline__ void finish(const State<T, D, PV>& st, const AttnArgs
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float lt = pair_sum(st.l[nt]);
+    const float ls = pair_sum(stat_sum<PV, TL::F32, STATS>(st.l[nt], st.lx[nt]));
     inv[nt] = 1.0f / lt;
     if (hf == 0 && qvalid[nt]) {
       const size_t ri = (size_t)h * N + tokq[nt];
-      if (a.stats) a.stats[ri] = make_float2(st.m[nt], inv[nt]);
-      if (a.lse) a.lse[ri] = (st.m[nt] + __log2f(lt)) * kLn2;
+      if (a.stats) a.stats[ri] = make_float2(st.m[nt], 1.0f / ls);
+      if (a.lse) a.lse[ri] = (st.m[nt] + __log2f(ls)) * kLn2;
     }
   }
   if constexpr (PV) {
@@ -560,10 +573,10 @@ void attn_kernel(AttnArgs a) {
   if (__builtin_amdgcn_ballot_w64(!ok)) {
     State<T, D, PV> so;
     state_init<T, D, PV>(so);
-    pass_online<T, D, GATHER, PV>(so, x, rq, tokq[0], tokq[1]);
-    finish<T, D, EPI, PV>(so, a, h, tokq, qvalid, lm, hf);
+    pass_online<T, D, GATHER, PV, !GATHER>(so, x, rq, tokq[0], tokq[1]);
+    finish<T, D, EPI, PV, !GATHER>(so, a, h, tokq, qvalid, lm, hf);
   } else {
-    finish<T, D, EPI, PV>(st, a, h, tokq, qvalid, lm, hf);
+    finish<T, D, EPI, PV, !GATHER>(st, a, h, tokq, qvalid, lm, hf);
   }
 }
 
@@ -601,7 +614,8 @@ template <int D, bool PV>
 struct LState {
   f32x16 o[2][LT<D>::VT];
   float m[2];
-  float l[2];
+  float l[2];   // normaliser of O (see row_sums)
+  float lx[2];  // exact sum for the row statistics when l is the packed one
 };
 
 // Keys of the NI entries this lane copies (entries NI*g + 0..NI-1 of the step).
@@ -661,7 +675,7 @@ __device__ __forceinline__ void lmask(f32x16 (&s)[2], int t0, int nkeys, int hf)
       if (t0 + 8 * (r >> 2) + 4 * hf + (r & 3) >= nkeys) s[nt][r] = -INFINITY;
 }
 
-template <int D, bool PV, bool EXACT_SUM>
+template <int D, bool PV, bool STATS>
 __device__ __forceinline__ void lprobs(LState<D, PV>& st, f32x16 (&s)[2], uint32_t (&pk)[2][8], float c) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -672,19 +686,7 @@ __device__ __forceinline__ void lprobs(LState<D, PV>& st, f32x16 (&s)[2], uint32
 #pragma unroll
       for (int i = 0; i < 8; ++i) pk[nt][i] = pack_bf16x2(s[nt][2 * i], s[nt][2 * i + 1]);
     }
-    if constexpr (EXACT_SUM) {
-      float ls = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ls += s[nt][r];
-      st.l[nt] += ls;
-    } else {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-      float ls = st.l[nt];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[nt][i]), one, ls, false);
-      st.l[nt] = ls;
-    }
+    row_sums<PV, false, STATS>(st.l[nt], st.lx[nt], s[nt], pk[nt]);
   }
 }
 
@@ -739,11 +741,10 @@ struct LCtx {
 // One step on stage `cur`.  DMA_NEXT: start the copies of step it+1 into `nxt`
 // (keys in kn) and load the keys of step it+2 into kn; FIRST: fix the offsets
 // from this step's maxima; LAST: mask entries past the key count.
-template <int D, bool GATHER, bool PV, bool FIRST, bool LAST, bool DMA_NEXT>
+template <int D, bool GATHER, bool PV, bool STATS, bool FIRST, bool LAST, bool DMA_NEXT>
 __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
                                       const LDSP char* cur, LDSP char* nxt, const LKeys<D>& kcur, LKeys<D>& knext,
                                       int it) {
-  constexpr bool EXACT = !GATHER || !PV;
   constexpr int NKL = GATHER ? LT<D>::NI / 4 : 0;        // key loads per step
   constexpr int NDMA = (PV ? 2 : 1) * LT<D>::NI;         // copy instructions per step
   // The copies of step it+1 (keys in kcur) and the key load of step it+2 go out
@@ -779,7 +780,7 @@ __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const
       st.m[nt] = pair_max(mx) * x.c + kMargin;
     }
   }
-  lprobs<D, PV, EXACT>(st, s, pk, x.c);
+  lprobs<D, PV, STATS>(st, s, pk, x.c);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (PV) lpv<D>(st, pk, vb);
 }
@@ -792,7 +793,7 @@ __device__ __forceinline__ void lstep(LState<D, PV>& st, const LCtx<D>& x, const
 //
 // FRESH: the pass starts the softmax (its first step fixes the offsets); false
 // when steps over other keys of the same queries came before it.
-template <int D, bool GATHER, bool PV, bool FRESH = true>
+template <int D, bool GATHER, bool PV, bool STATS, bool FRESH = true>
 __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
                                       LDSP char* s0, LDSP char* s1) {
   const int nsteps = (x.nkeys + 31) >> 5;
@@ -801,21 +802,21 @@ __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const
   ldma<D, PV>(s0, ka, x.rk, x.rv, x.goff);
   lkeys<D, GATHER>(kb, x.ridx, 32, x.ebase);
   if (nsteps == 1) {
-    lstep<D, GATHER, PV, FRESH, true, false>(st, x, q, s0, s1, kb, ka, 0);
+    lstep<D, GATHER, PV, STATS, FRESH, true, false>(st, x, q, s0, s1, kb, ka, 0);
     return;
   }
-  lstep<D, GATHER, PV, FRESH, false, true>(st, x, q, s0, s1, kb, ka, 0);
+  lstep<D, GATHER, PV, STATS, FRESH, false, true>(st, x, q, s0, s1, kb, ka, 0);
   int it = 1;
   for (; it + 2 < nsteps; it += 2) {
-    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, ka, kb, it);
-    lstep<D, GATHER, PV, false, false, true>(st, x, q, s0, s1, kb, ka, it + 1);
+    lstep<D, GATHER, PV, STATS, false, false, true>(st, x, q, s1, s0, ka, kb, it);
+    lstep<D, GATHER, PV, STATS, false, false, true>(st, x, q, s0, s1, kb, ka, it + 1);
   }
   // it is odd: stage s1 holds step it
   if (it + 1 < nsteps) {
-    lstep<D, GATHER, PV, false, false, true>(st, x, q, s1, s0, ka, kb, it);
-    lstep<D, GATHER, PV, false, true, false>(st, x, q, s0, s1, kb, ka, it + 1);
+    lstep<D, GATHER, PV, STATS, false, false, true>(st, x, q, s1, s0, ka, kb, it);
+    lstep<D, GATHER, PV, STATS, false, true, false>(st, x, q, s0, s1, kb, ka, it + 1);
   } else {
-    lstep<D, GATHER, PV, false, true, false>(st, x, q, s1, s0, ka, kb, it);
+    lstep<D, GATHER, PV, STATS, false, true, false>(st, x, q, s1, s0, ka, kb, it);
   }
 }
 
@@ -823,7 +824,7 @@ __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const
 // (fp32, one half of the group at a time) so that every lane stores 16
 // contiguous bytes of one output row, and the residual is added in fp32 before
 // the single rounding to bf16.
-template <int D, int EPI, bool PV>
+template <int D, int EPI, bool PV, bool STATS>
 __device__ __forceinline__ void lfinish(const LState<D, PV>& st, const AttnArgs& a, int h, const int (&tokq)[2],
                                         const bool (&qvalid)[2], int lane, LDSP char* buf) {
   using L = LT<D>;
@@ -832,11 +833,12 @@ __device__ __forceinline__ void lfinish(const LState<D, PV>& st, const AttnArgs&
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float lt = pair_sum(st.l[nt]);
+    const float ls = pair_sum(stat_sum<PV, false, STATS>(st.l[nt], st.lx[nt]));
     inv[nt] = 1.0f / lt;
     if (hf == 0 && qvalid[nt]) {
       const size_t ri = (size_t)h * N + tokq[nt];
-      if (a.stats) a.stats[ri] = make_float2(st.m[nt], inv[nt]);
-      if (a.lse) a.lse[ri] = (st.m[nt] + __log2f(lt)) * kLn2;
+      if (a.stats) a.stats[ri] = make_float2(st.m[nt], 1.0f / ls);
+      if (a.lse) a.lse[ri] = (st.m[nt] + __log2f(ls)) * kLn2;
     }
   }
   if constexpr (PV) {
@@ -964,6 +966,7 @@ __device__ __forceinline__ void lstate_init(LState<D, PV>& st) {
   for (int nt = 0; nt < 2; ++nt) {
     st.m[nt] = 0.0f;
     st.l[nt] = 0.0f;
+    st.lx[nt] = 0.0f;
     if constexpr (PV) {
 #pragma unroll
       for (int n = 0; n < LT<D>::VT; ++n) st.o[nt][n] = f32x16{};
@@ -974,7 +977,7 @@ __device__ __forceinline__ void lstate_init(LState<D, PV>& st) {
 // Normalise and store, or, if a logit far above its query's first-tile maximum
 // overflowed the fixed offset, redo the group with the online pass (direct
 // global loads over the whole key list of x.ridx).
-template <int D, bool GATHER, int EPI, bool PV>
+template <int D, bool GATHER, int EPI, bool PV, bool STATS>
 __device__ __forceinline__ void lend(const LState<D, PV>& st, const LCtx<D>& x, const AttnArgs& a,
                                      __amdgpu_buffer_rsrc_t rq, int h, const int (&tokq)[2],
                                      const bool (&qvalid)[2], int lane, LDSP char* buf) {
@@ -991,14 +994,16 @@ __device__ __forceinline__ void lend(const LState<D, PV>& st, const LCtx<D>& x, 
     xo.c = x.c;
     State<__bf16, D, PV> so;
     state_init<__bf16, D, PV>(so);
-    pass_online<__bf16, D, GATHER, PV>(so, xo, rq, tokq[0], tokq[1]);
-    finish<__bf16, D, EPI, PV>(so, a, h, tokq, qvalid, lm, hf);
+    pass_online<__bf16, D, GATHER, PV, STATS>(so, xo, rq, tokq[0], tokq[1]);
+    finish<__bf16, D, EPI, PV, STATS>(so, a, h, tokq, qvalid, lm, hf);
   } else {
-    lfinish<D, EPI, PV>(st, a, h, tokq, qvalid, lane, buf);
+    lfinish<D, EPI, PV, STATS>(st, a, h, tokq, qvalid, lane, buf);
   }
 }
 
-template <int D, bool GATHER, int EPI, bool PV>
+// STATS (dense with PV only): also keep the exact row sums for the statistics;
+// the other variants have one sum (see row_sums).
+template <int D, bool GATHER, int EPI, bool PV, bool STATS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_lds_kernel(AttnArgs a) {
   using L = LT<D>;
@@ -1024,8 +1029,8 @@ void attn_lds_kernel(AttnArgs a) {
   lzero<D>(s0, s1, lane);
   LState<D, PV> st;
   lstate_init<D, PV>(st);
-  if (x.nkeys > 0) lpass<D, GATHER, PV>(st, x, q, s0, s1);
-  lend<D, GATHER, EPI, PV>(st, x, a, rq, h, tokq, qvalid, lane, s0);
+  if (x.nkeys > 0) lpass<D, GATHER, PV, STATS>(st, x, q, s0, s1);
+  lend<D, GATHER, EPI, PV, STATS>(st, x, a, rq, h, tokq, qvalid, lane, s0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1163,18 +1168,18 @@ void attn_pairs_kernel(AttnArgs a, const int32_t* ncommon) {
     xp.ridx = make_rsrc(a.idx + ((size_t)h * a.G + g) * a.kpad + nc, (uint32_t)(a.kpad - nc) * 4u);
     xp.nkeys = npriv;
     if (ns == 0)
-      lpass<D, true, true, true>(st, xp, q, own0, own1);
+      lpass<D, true, true, false, true>(st, xp, q, own0, own1);
     else
-      lpass<D, true, true, false>(st, xp, q, own0, own1);
+      lpass<D, true, true, false, false>(st, xp, q, own0, own1);
   }
-  lend<D, true, EPI, true>(st, x, a, rq, h, tokq, qvalid, lane, own0);
+  lend<D, true, EPI, true, false>(st, x, a, rq, h, tokq, qvalid, lane, own0);
 }
 
-template <int D, bool GATHER, int EPI, bool PV>
+template <int D, bool GATHER, int EPI, bool PV, bool STATS = false>
 hipError_t launch_lds(const AttnArgs& a, hipStream_t s) {
   const int items = a.H * a.G;
   const int blocks = xcd_grid((items + 3) / 4);
-  hipLaunchKernelGGL((attn_lds_kernel<D, GATHER, EPI, PV>), dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_lds_kernel<D, GATHER, EPI, PV, STATS>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1213,7 +1218,9 @@ hipError_t launch_d(const AttnArgs& a, bool gather, int epi, bool pv, hipStream_
         default: return launch_lds<D, true, EPI_PLAIN, true>(a, s);
       }
     }
-    return launch_lds<D, false, EPI_PLAIN, true>(a, s);
+    // dense: the exact row sums are kept only when statistics are written
+    return (a.stats || a.lse) ? launch_lds<D, false, EPI_PLAIN, true, true>(a, s)
+                              : launch_lds<D, false, EPI_PLAIN, true, false>(a, s);
   } else {
     if (!pv) return gather ? launch_t<T, D, true, EPI_PLAIN, false>(a, s) : launch_t<T, D, false, EPI_PLAIN, false>(a, s);
     if (gather) {

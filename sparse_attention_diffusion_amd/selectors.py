@@ -76,7 +76,7 @@ def run(grid=(20, 45, 80), heads=8, density=0.2, steps=4, drift=0.02, seed=5, de
         o_s = mcs.mcs_sparse_attn(q, k, v, perm, idx, kk)
         lse_s = mcs.mcs_sparse_lse(q, k, perm, idx, kk)
         cap = torch.exp(lse_s - lse_dense)
-        resid[name] = (o_dense.float() - o_s.float()).to(q.dtype)
+        resid[name] = mcs.mcs_residual(q, k, v, perm, idx, kk, o_dense)
         out["selectors"][name] = {"captured_mass_mean": round(cap.mean().item(), 5),
                                   "captured_mass_p10": round(torch.quantile(cap.flatten()[::97].float(), 0.1).item(), 5),
                                   "anchor_error": _errors(o_s, o_dense), "reuse": []}

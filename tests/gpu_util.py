@@ -68,3 +68,62 @@ def random_groups(n, k, heads, seed, c=64):
         for gi in range(g):
             idx[h, gi, :k] = np.sort(r.choice(n, k, replace=False))
     return perm, idx
+
+
+# Error bound of a bf16 attention output against fp64, per element.  The kernel
+# multiplies V by the probabilities rounded to bf16 (relative error <= 2^-8 each)
+# and divides by the sum of those same rounded values, so the weights it applies
+# are w~_j = w_j (1 + e_j) / (1 + sum_k w_k e_k), |e_j| <= 2^-8, and
+#   O~ - O = sum_j w_j (e_j - e) (v_j - O) / (1 + e),  |e_j - e| <= 2^-7,
+# i.e. |O~ - O| <= 2^-7 (1 + 2^-7) sum_j w_j |v_j - O| per output dimension.  The
+# fp32 accumulation adds a few 2^-24 relative, and the single rounding of the
+# result to bf16 adds half a bf16 ulp of the result.
+P_ROUND = 2.0 ** -7 * (1.0 + 2.0 ** -7)
+
+
+def attention_spread(q, k, v, rows, keys, scale, block=64):
+    """fp64 (O, spread) of the given query rows over `keys` (an index array shared by
+    all rows): spread[i, d] = sum_j w_ij |v_jd - O_id|."""
+    q = np.asarray(q, np.float64)
+    kk = np.asarray(k, np.float64)[keys]
+    vv = np.asarray(v, np.float64)[keys]
+    rows = np.asarray(rows)
+    o = np.empty((len(rows), vv.shape[1]))
+    sp = np.empty_like(o)
+    for b in range(0, len(rows), block):
+        z = scale * (q[rows[b:b + block]] @ kk.T)
+        w = np.exp(z - z.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        ob = w @ vv
+        o[b:b + block] = ob
+        sp[b:b + block] = np.einsum("ij,ijd->id", w, np.abs(vv[None, :, :] - ob[:, None, :]))
+    return o, sp
+
+
+def bf16_attention_bound(o, spread, slack=1e-5):
+    """Per-element bound on |bf16 kernel output - fp64 O| (see P_ROUND)."""
+    dev_ = P_ROUND * spread + slack * (1.0 + np.abs(o))
+    return dev_ + bf16_half_ulp(np.abs(o) + dev_)
+
+
+def assert_within(got, want, bound, what=""):
+    err = np.abs(np.asarray(got, np.float64) - want)
+    over = err > bound
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert not over.any(), (f"{what}: {int(over.sum())} elements above the derived bound; worst "
+                            f"err {float(err[over].max()):.3e} vs bound {float(bound[over][np.argmax(err[over])]):.3e}")
+    return float(err.max())
+
+
+def check_index_row_window(row, mass, k, n, rel):
+    """check_index_row with a wider relative tie window `rel` (for logits large enough
+    that their fp32 rounding moves exp() by more than 1e-6 relative)."""
+    row = np.asarray(row)
+    kept, pad = row[:k], row[k:]
+    assert (pad == -1).all() and ((kept >= 0) & (kept < n)).all() and (np.diff(kept) > 0).all()
+    want = ref.topk_from_mass(mass, k)
+    tau = np.sort(mass)[::-1][k - 1]
+    diff = np.setxor1d(kept, want)
+    bad = [j for j in diff if abs(mass[j] - tau) > rel * tau]
+    assert not bad, f"{len(bad)} keys differ beyond ties (tau={tau:.6e}, rel={rel:.2e}): {bad[:8]}"
+    return len(diff)

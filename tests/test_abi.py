@@ -157,3 +157,15 @@ def test_block_select_and_sparse_lse_reject_bad_args(lib):
         == _abi.MCS_EWORKSPACE
     assert lib.mcs_sparse_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) == _abi.MCS_EINVAL
     assert b"lse" in lib.mcs_last_error()
+
+
+def test_residual_rejects_bad_args(lib):
+    d = _dims()
+    other = ctypes.c_void_p(1 << 21)
+    args = lambda od, r: [FAKE, FAKE, FAKE, FAKE, FAKE, od, r, None]  # q k v perm idx o_dense resid stream
+    assert lib.mcs_residual(ctypes.byref(d), *args(FAKE, FAKE)) == _abi.MCS_EINVAL
+    assert b"alias" in lib.mcs_last_error()
+    assert lib.mcs_residual(ctypes.byref(d), *args(None, other)) == _abi.MCS_EINVAL
+    assert b"o_dense" in lib.mcs_last_error()
+    assert lib.mcs_residual(ctypes.byref(_dims(topk=0)), *args(FAKE, other)) == _abi.MCS_EINVAL
+    assert lib.mcs_residual(ctypes.byref(_dims(head_dim=80)), *args(FAKE, other)) == _abi.MCS_EUNSUPPORTED
