@@ -113,6 +113,23 @@ int mcs_group(const mcs_dims* d, const void* q, int32_t* perm, void* ws, size_t 
 int mcs_select(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const float* lse,
                int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* mcs_select without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same result as mcs_select (bit for bit); the row
+ * statistics and mass rows live in a static device array of MCS_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends.  Processes
+ * ceil(H / hpp) passes of hpp heads, hpp as large as the scratch allows.
+ * Workloads needing more than MCS_SCRATCH_BYTES for one head (8*H*N bytes of
+ * statistics plus about N*N/16 of mass rows, padded) are rejected with
+ * MCS_EUNSUPPORTED before any HIP call.  The scratch belongs to the current
+ * device (hipSetDevice), which must be the device of `stream` and of every
+ * buffer.  Every call on one GPU shares that GPU's scratch: calls that overlap
+ * in time on one GPU (other streams, other threads) race.  Allocates nothing:
+ * no hipMalloc, hipFree or allocating library routine. */
+#define MCS_SCRATCH_BYTES ((size_t)128 << 20)
+int mcs_select_noalloc(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const float* lse,
+                       int32_t* idx, hipStream_t stream);
+
 /* Dense softmax attention (summary page, limitations paragraph: anchors run full
  * attention): o[h][i] = sum_j softmax_j(scale*q_i.k_j) v[h][j].  Writes o and,
  * when lse is non-NULL, the row logsumexp. */

@@ -174,6 +174,24 @@ def mcs_select(q, k, perm, topk: int, lse=None, ws=None, heads_per_pass: int = 0
     return idx
 
 
+def mcs_select_noalloc(q, k, perm, topk: int, lse=None, idx=None):
+    """mcs_select without a workspace: the library's static device scratch holds the
+    selection's intermediates (no device allocation inside the call when idx is given)."""
+    torch = _torch()
+    lib = _abi.load()
+    _check_same(q, k)
+    d = make_dims(q, topk=topk)
+    if idx is None:
+        idx = torch.empty((q.shape[0], _groups(q.shape[1]), d.kpad), dtype=torch.int32, device=q.device)
+    d.kpad = _check_idx(idx, q, topk)
+    _check_perm(perm, q)
+    _check_lse(lse, q)
+    _check_gpu(q)
+    _abi.check(lib.mcs_select_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(perm), _ptr(lse), _ptr(idx),
+                                      _stream(q.device)))
+    return idx
+
+
 def mcs_dense_attn(q, k, v, want_lse: bool = False, o=None):
     """Dense attention: returns (o, lse or None)."""
     torch = _torch()

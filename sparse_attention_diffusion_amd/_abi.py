@@ -13,11 +13,12 @@ MCS_OP_GROUP, MCS_OP_SELECT, MCS_OP_ANCHOR, MCS_OP_BLOCK_SELECT = 1, 2, 3, 4
 MCS_COPY_H2D, MCS_COPY_D2H, MCS_COPY_D2D = 1, 2, 3
 ABI_VERSION = 1
 
-EXPORTED = ("mcs_abi_version", "mcs_last_error", "mcs_workspace_bytes", "mcs_group", "mcs_select",
+EXPORTED = ("mcs_abi_version", "mcs_last_error", "mcs_workspace_bytes", "mcs_group", "mcs_select", "mcs_select_noalloc",
             "mcs_dense_attn", "mcs_sparse_attn", "mcs_anchor", "mcs_residual", "mcs_reuse", "mcs_idx_to_bits", "mcs_bits_to_idx",
             "mcs_pair_plan", "mcs_sparse_attn_pairs", "mcs_block_select", "mcs_sparse_lse", "mcs_copy_async")
 BITS_MAX_N = 1 << 20
 PAIRS_MAX_N = 1 << 19
+SCRATCH_BYTES = 128 << 20
 
 
 class McsDims(ctypes.Structure):
@@ -52,6 +53,7 @@ def load():
         "mcs_workspace_bytes": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "mcs_group": (ctypes.c_int, [D, P, P, P, S, St]),
         "mcs_select": (ctypes.c_int, [D, P, P, P, P, P, P, S, St]),
+        "mcs_select_noalloc": (ctypes.c_int, [D, P, P, P, P, P, St]),
         "mcs_dense_attn": (ctypes.c_int, [D, P, P, P, P, P, St]),
         "mcs_sparse_attn": (ctypes.c_int, [D, P, P, P, P, P, P, P, St]),
         "mcs_anchor": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, S, St]),

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/mcs.h"
@@ -125,6 +126,35 @@ int heads_per_pass(const mcs_dims* d, size_t ws_bytes) {
   return hpp > (size_t)d->heads ? d->heads : (int)hpp;
 }
 
+// Device-resident scratch of mcs_select_noalloc (for callers that cannot
+// allocate).  In host code `scratch` names a host-side stand-in, not device
+// memory: only the address hipGetSymbolAddress returns for the current device
+// is ever handed to a kernel.  Each GPU the library runs on holds its own copy
+// until the process ends.
+static __device__ __align__(256) unsigned char scratch[MCS_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MCS_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MCS_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MCS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,6 +217,28 @@ int mcs_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
     if (e != hipSuccess) return hip_fail(e, "selection pass 1 launch");
   }
   return run_select(d, q, k, perm, lse ? nullptr : stats, lse, idx, mass, hpp, stream);
+}
+
+int mcs_select_noalloc(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const float* lse,
+                       int32_t* idx, hipStream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(d, true));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(perm, 4, "perm"));
+  CHECK(check_ptr(idx, 16, "idx"));
+  if (lse) CHECK(check_ptr(lse, 4, "lse"));
+  // sizes first: a workload the scratch cannot hold is rejected before any HIP call
+  const size_t need = select_ws(d, 1);
+  if (need > (size_t)MCS_SCRATCH_BYTES)
+    return fail(MCS_EUNSUPPORTED, "selection of n=%d needs %zu bytes of scratch for one head, above the %zu the "
+                "library holds (use mcs_select with a workspace)", d->n, need, (size_t)MCS_SCRATCH_BYTES);
+  void* ws = nullptr;
+  CHECK(scratch_address(&ws));
+  // Every byte the kernels read from the scratch is written earlier in the same
+  // call (row statistics by pass 1 for every token, each mass row by the wave
+  // that then reads it), so nothing left by an earlier call needs clearing.
+  return mcs_select(d, q, k, perm, lse, idx, ws, (size_t)MCS_SCRATCH_BYTES, stream);
 }
 
 int mcs_dense_attn(const mcs_dims* d, const void* q, const void* k, const void* v, void* o, float* lse,

@@ -169,3 +169,12 @@ def test_residual_rejects_bad_args(lib):
     assert b"o_dense" in lib.mcs_last_error()
     assert lib.mcs_residual(ctypes.byref(_dims(topk=0)), *args(FAKE, other)) == _abi.MCS_EINVAL
     assert lib.mcs_residual(ctypes.byref(_dims(head_dim=80)), *args(FAKE, other)) == _abi.MCS_EUNSUPPORTED
+
+
+def test_select_noalloc_checks_sizes_before_any_hip_call(lib):
+    # 50,000 tokens: one head of mass rows is 782 x 50,000 x 4 bytes > the 128 MiB scratch
+    big = _dims(heads=1, n=50000, head_dim=64, topk=100, kpad=128)
+    assert lib.mcs_select_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, None, FAKE, None) == _abi.MCS_EUNSUPPORTED
+    assert b"scratch" in lib.mcs_last_error()
+    assert lib.mcs_select_noalloc(ctypes.byref(_dims()), FAKE, FAKE, None, None, FAKE, None) == _abi.MCS_EINVAL
+    assert lib.mcs_select_noalloc(ctypes.byref(_dims(topk=0)), FAKE, FAKE, FAKE, None, FAKE, None) == _abi.MCS_EINVAL
