@@ -15,7 +15,11 @@ From the measured times of the anchor entry point, the reuse step and dense
 attention it derives, for anchor gaps g = 1..T+1, the cost of a step averaged over
 one gap, (t_anchor + (g - 1) t_reuse) / g, as an effective density (that cost
 over t_dense), and the overhead in density points, (effective density - density)
-* 100.
+* 100.  The warm-up sweep applies the same costs to a whole trajectory of S
+steps (S = 50 by default) that starts with W dense warm-up steps and then runs
+an anchor every g steps: speed-up against S dense steps and the overhead of the
+sparse steps in density points, ((cost / t_dense) - W - (S - W) * density) /
+(S - W) * 100, the figure the trajectory harness reports.
 
 Usage: python -m sparse_attention_diffusion_amd.drift [--workload NAME] [--density RHO]
        [--steps T] [--drift SIGMA] [--heads H]
@@ -38,7 +42,26 @@ def _mean_max(a, b):
     return round(d.mean().item(), 6), round(d.max().item(), 5)
 
 
-def run(workload="hunyuan_trajectory", density=0.15, steps=25, drift=None, heads=None, reps=3, device="cuda:0"):
+WARMUPS = (0, 1, 2, 5, 10, 15)
+GAPS = (1, 2, 3, 5, 8, 10, 15, 20, 25)
+
+
+def schedule_cost(t_dense, t_anchor, t_reuse, total_steps, warmup, gap, density):
+    """Attention cost of a trajectory: `warmup` dense steps, then an anchor every
+    `gap` steps and reuse steps in between.  Returns (speed-up against all-dense,
+    overhead of the sparse steps in density points)."""
+    sparse = total_steps - warmup
+    anchors = -(-sparse // gap) if sparse > 0 else 0
+    cost = warmup * t_dense + anchors * t_anchor + (sparse - anchors) * t_reuse
+    speedup = total_steps * t_dense / cost
+    overhead = ((cost / t_dense - warmup - sparse * density) / sparse * 100.0) if sparse > 0 else float("nan")
+    return speedup, overhead
+
+
+def run(workload="hunyuan_trajectory", density=0.15, steps=25, drift=None, heads=None, reps=3, device="cuda:0",
+        capture=None, total_steps=50):
+    """capture: optional dict that receives the anchor's device tensors (perm, idx,
+    resid, o_dense) for checks against the oracle."""
     import dataclasses
 
     import torch
@@ -56,6 +79,8 @@ def run(workload="hunyuan_trajectory", density=0.15, steps=25, drift=None, heads
     q, k, v = W.make_qkv_torch(wl, dev)
     anchor = mcs.mcs_anchor(q, k, v, kk)
     perm, idx, r0, o0 = anchor["perm"], anchor["idx"], anchor["resid"], anchor["o_dense"]
+    if capture is not None:
+        capture.update(perm=perm, idx=idx, resid=r0, o_dense=o0)
 
     def timed(fn):
         fn()
@@ -101,6 +126,12 @@ def run(workload="hunyuan_trajectory", density=0.15, steps=25, drift=None, heads
         eff = per_step / t_dense
         res["gap"].append({"gap": g, "effective_density": round(eff, 4), "overhead_points": round((eff - density) * 100, 2),
                            "speedup_vs_dense": round(1.0 / eff, 3)})
+    res["warmup_sweep"] = []
+    for w in WARMUPS:
+        for g in GAPS:
+            sp_, ov = schedule_cost(t_dense, t_anchor, t_reuse, total_steps, w, g, density)
+            res["warmup_sweep"].append({"steps": total_steps, "warmup": w, "gap": g, "speedup_vs_dense": round(sp_, 3),
+                                        "overhead_points": round(ov, 2)})
     torch.cuda.synchronize()
     return res
 
@@ -125,6 +156,10 @@ def main(argv=None):
                   f"{s['no_residual_mean_abs']:.2e}); residual moved {s['resid_change_rel']:.3f}, output "
                   f"{s['output_change_rel']:.3f}; gap {g['gap']}: {g['overhead_points']:.1f} density points, "
                   f"{g['speedup_vs_dense']:.2f}x dense", file=sys.stderr)
+    for row in res["warmup_sweep"]:
+        if row["gap"] in (5, 10, 25):
+            print(f"[drift] {row['steps']} steps, warm-up {row['warmup']:2d}, gap {row['gap']:2d}: "
+                  f"{row['speedup_vs_dense']:.2f}x dense, {row['overhead_points']:.1f} density points", file=sys.stderr)
 
 
 if __name__ == "__main__":

@@ -29,27 +29,34 @@ def step_kind(step, warmup, interval):
 
 
 class LayerInputs:
-    """Q/K/V of every layer on the device, advanced by one random-walk step at a time."""
+    """Q/K/V of every layer: float32 masters on the device, advanced by one
+    random-walk step at a time and rounded once into the storage-dtype buffers a
+    layer call reads, so that layer l at step t holds exactly
+    ``make_qkv_torch(wl, step=t, layer=l)`` (drift applied before rounding)."""
 
     def __init__(self, wl, layers, device):
-        import torch
-        from .workloads import make_qkv_torch
-        self.torch = torch
+        from .workloads import base_qkv_torch, storage_dtype_torch
         self.wl = wl
         self.device = device
-        self.state = [make_qkv_torch(wl, device, layer=l) for l in range(layers)]
-        self.step = 0
+        self.master = [base_qkv_torch(wl, device, layer=l) for l in range(layers)]
+        dt = storage_dtype_torch(wl)
+        self.work = tuple(torch_empty_like(self.master[0][0], dt) for _ in range(3))
 
     def advance(self, layer, step):
-        torch = self.torch
-        g = torch.Generator(device=self.device)
-        g.manual_seed(int(np.random.SeedSequence([self.wl.seed, layer, 1 << 20, step]).generate_state(1)[0]))
-        for t in self.state[layer]:
-            t.add_(torch.randn(t.shape, generator=g, device=self.device, dtype=torch.float32)
-                   .mul_(self.wl.drift_sigma).to(t.dtype))
+        from .workloads import drift_torch_
+        drift_torch_(*self.master[layer], self.wl, layer, step)
 
     def get(self, layer):
-        return self.state[layer]
+        """Storage-dtype Q, K, V of `layer` at its current step (shared buffers: valid
+        until the next call)."""
+        for w, m in zip(self.work, self.master[layer]):
+            w.copy_(m)
+        return self.work
+
+
+def torch_empty_like(t, dtype):
+    import torch
+    return torch.empty(t.shape, dtype=dtype, device=t.device)
 
 
 def entry_bytes(wl, density, compact):
@@ -63,16 +70,23 @@ def entry_bytes(wl, density, compact):
 
 
 def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, device_slots=2, heads_per_pass=4,
-        record_outputs=None, log=None, compact=False, resident_layers=0):
+        record_outputs=None, log=None, compact=False, resident_layers=0, pinned_budget=None, record_inputs=None,
+        record_entries=None):
     """compact: cache the kept-key sets as per-group key bitmaps (encoded after
     each anchor, decoded before each reuse into one shared list buffer).
     resident_layers: with offload, the first that many layers keep their entries
     on the device (the layers that fit a memory budget); only the rest are
-    offloaded."""
+    offloaded.  pinned_budget: bytes of pinned host memory for the offloaded
+    entries (default: the cache's), pageable beyond.
+    record_outputs / record_inputs: dicts keyed by (step, layer) whose values are
+    filled with the layer call's output / its (q, k, v) on the device;
+    record_entries: dict filled, at every anchor of a (step, layer) key present
+    in it, with the cache entry the anchor wrote ({"perm", "idx", "resid"}, idx
+    decoded when compact)."""
     import torch
 
     import sparse_attention_diffusion_amd as mcs
-    from .cache import MetaCache, TorchBackend
+    from .cache import DEFAULT_PINNED_BUDGET, MetaCache, TorchBackend
 
     dev = torch.device("cuda:0")
     kk = wl.topk(density)
@@ -90,7 +104,8 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
                   "resid": ((h, n, dd), q0.dtype)}
     be = TorchBackend(dev)
     cache = MetaCache(layers, shapes, be, offload=offload, device_slots=device_slots,
-                      resident_layers=resident_layers)
+                      resident_layers=resident_layers,
+                      pinned_budget=DEFAULT_PINNED_BUDGET if pinned_budget is None else pinned_budget)
     ws = torch.empty(mcs.mcs_workspace_bytes(d, mcs.MCS_OP_ANCHOR, heads_per_pass), dtype=torch.uint8, device=dev)
     o_dense = torch.empty_like(q0)
     out = torch.empty_like(q0)
@@ -117,6 +132,10 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
                 mcs.mcs_anchor(q, k, v, kk, ws=ws, heads_per_pass=heads_per_pass, out=res)
                 if compact:
                     mcs.mcs_idx_to_bits(idx_scratch, n, kk, bits=buf["bits"])
+                if record_entries is not None and (step, layer) in record_entries:
+                    idx_rec = mcs.mcs_bits_to_idx(buf["bits"], n, kk, kpad=d.kpad) if compact else buf["idx"]
+                    record_entries[(step, layer)] = {"perm": buf["perm"].clone(), "idx": idx_rec.clone(),
+                                                     "resid": buf["resid"].clone()}
                 cache.commit_anchor(layer)
                 cache.release(layer)
             else:
@@ -132,11 +151,15 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
                 cache.prefetch(nxt_layer, busy_layer=layer)
             if record_outputs is not None and (step, layer) in record_outputs:
                 record_outputs[(step, layer)] = (o_dense if kind == "anchor" else out).clone()
+            if record_inputs is not None and (step, layer) in record_inputs:
+                record_inputs[(step, layer)] = tuple(t.clone() for t in (q, k, v))
         if log:
             torch.cuda.synchronize()
             log(f"[trajectory] step {step + 1}/{steps} ({kind}) done")
+    cache.drain()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    be.close()
     ms = {kk_: [x.elapsed_time(y) for x, y in v_] for kk_, v_ in times.items()}
     t_dense_call = float(np.mean(ms["dense"])) if ms["dense"] else float("nan")
     total_attn = sum(sum(v_) for v_ in ms.values())
@@ -162,6 +185,8 @@ def run(wl, layers, steps, warmup=5, interval=5, density=0.15, offload=False, de
         "cache_bytes_per_layer": sum(math.prod(s_) * torch.empty((), dtype=t_).element_size()
                                      for s_, t_ in shapes.values()),
         "bytes_d2h": cache.bytes_d2h, "bytes_h2d": cache.bytes_h2d,
+        "host_pinned_bytes": cache.host_pinned_bytes, "host_pageable_bytes": cache.host_pageable_bytes,
+        "host_wait_s": round(cache.host_wait_s, 3),
         "h2d_gbps_if_serial": round(cache.bytes_h2d / 1e9 / wall, 2) if wall > 0 else None,
     }
 
@@ -180,6 +205,8 @@ def main():
     ap.add_argument("--heads-per-pass", type=int, default=4)
     ap.add_argument("--resident-gb", type=float, default=0.0,
                     help="with --offload: keep resident as many layers' entries as fit in this many GB")
+    ap.add_argument("--pinned-gb", type=float, default=None,
+                    help="with --offload: pinned host memory for the offloaded entries (GiB), pageable beyond")
     args = ap.parse_args()
     wl = WORKLOADS[args.workload]
     resident = 0
@@ -187,7 +214,8 @@ def main():
         resident = min(args.layers, int(args.resident_gb * 1e9 // entry_bytes(wl, args.density, args.compact)))
     res = run(wl, args.layers, args.steps, args.warmup, args.interval, args.density, args.offload,
               heads_per_pass=args.heads_per_pass, log=lambda m: print(m, file=sys.stderr, flush=True),
-              compact=args.compact, resident_layers=resident)
+              compact=args.compact, resident_layers=resident,
+              pinned_budget=None if args.pinned_gb is None else int(args.pinned_gb * (1 << 30)))
     print(json.dumps(res), flush=True)
 
 

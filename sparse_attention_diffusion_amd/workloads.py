@@ -152,38 +152,63 @@ def make_qkv(wl: Workload, step: int = 0, layer: int = 0, heads=None, noise: flo
     return tuple(np.stack(o) for o in out)
 
 
+def _torch_gen(device, *key):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence(list(key)).generate_state(1)[0]))
+    return g
+
+
+def base_qkv_torch(wl: Workload, device, layer: int = 0, noise: float = 0.5, heads=None):
+    """Un-rounded float32 (H, N, D) Q, K, V of one layer at step 0, drawn on a torch
+    device (same recipe as ``make_qkv``; per head one torch.Generator stream seeded
+    from (seed, layer, head, 0))."""
+    import torch
+
+    coords = torch.from_numpy(grid_coords(wl.grid)).to(device=device, dtype=torch.float32)
+    n, d = coords.shape[0], wl.head_dim
+    hs = list(range(wl.heads)) if heads is None else list(heads)
+    out = [torch.empty((len(hs), n, d), device=device, dtype=torch.float32) for _ in range(3)]
+    for i, h in enumerate(hs):
+        g = _torch_gen(device, wl.seed, layer, h, 0)
+        w = torch.randn((3, d), generator=g, device=device)
+        b = torch.rand((d,), generator=g, device=device) * (2.0 * math.pi)
+        f = math.sqrt(2.0) * torch.cos(coords @ w + b)
+        out[0][i] = f + noise * torch.randn((n, d), generator=g, device=device)
+        out[1][i] = f + noise * torch.randn((n, d), generator=g, device=device)
+        out[2][i] = torch.randn((n, d), generator=g, device=device)
+    return tuple(out)
+
+
+def drift_torch_(q, k, v, wl: Workload, layer: int, step: int, heads=None):
+    """Advance float32 (H, N, D) Q, K, V of one layer in place by the random-walk
+    step `step` (>= 1): per head one generator seeded from (seed, layer, head, step)."""
+    import torch
+
+    hs = list(range(q.shape[0])) if heads is None else list(heads)
+    n, d = q.shape[1], q.shape[2]
+    for i, h in enumerate(hs):
+        gs = _torch_gen(q.device, wl.seed, layer, h, step)
+        for t in (q, k, v):
+            t[i] += wl.drift_sigma * torch.randn((n, d), generator=gs, device=q.device)
+
+
+def storage_dtype_torch(wl: Workload):
+    import torch
+    return torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+
 def make_qkv_torch(wl: Workload, device, step: int = 0, layer: int = 0, noise: float = 0.5,
                    heads=None):
     """Draw (H, N, D) Q, K, V directly on a torch device (large workloads).
 
     Same recipe as ``make_qkv`` with torch.Generator streams seeded from
-    (seed, layer, head, step); returned in the storage dtype (float32 / bfloat16).
+    (seed, layer, head, step): the float32 base (``base_qkv_torch``), then the
+    drift of steps 1..step (``drift_torch_``) before the single rounding to the
+    storage dtype (float32 / bfloat16).
     """
-    import torch
-
-    t_dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-    coords = torch.from_numpy(grid_coords(wl.grid)).to(device=device, dtype=torch.float32)
-    n, d = coords.shape[0], wl.head_dim
-    hs = list(range(wl.heads)) if heads is None else list(heads)
-    qs = torch.empty((len(hs), n, d), device=device, dtype=t_dtype)
-    ks = torch.empty_like(qs)
-    vs = torch.empty_like(qs)
-    for i, h in enumerate(hs):
-        g = torch.Generator(device=device)
-        g.manual_seed(int(np.random.SeedSequence([wl.seed, layer, h, 0]).generate_state(1)[0]))
-        w = torch.randn((3, d), generator=g, device=device)
-        b = torch.rand((d,), generator=g, device=device) * (2.0 * math.pi)
-        f = math.sqrt(2.0) * torch.cos(coords @ w + b)
-        q = f + noise * torch.randn((n, d), generator=g, device=device)
-        k = f + noise * torch.randn((n, d), generator=g, device=device)
-        v = torch.randn((n, d), generator=g, device=device)
-        for s in range(1, step + 1):
-            gs = torch.Generator(device=device)
-            gs.manual_seed(int(np.random.SeedSequence([wl.seed, layer, h, s]).generate_state(1)[0]))
-            q += wl.drift_sigma * torch.randn((n, d), generator=gs, device=device)
-            k += wl.drift_sigma * torch.randn((n, d), generator=gs, device=device)
-            v += wl.drift_sigma * torch.randn((n, d), generator=gs, device=device)
-        qs[i].copy_(q)
-        ks[i].copy_(k)
-        vs[i].copy_(v)
-    return qs, ks, vs
+    q, k, v = base_qkv_torch(wl, device, layer, noise, heads)
+    for s in range(1, step + 1):
+        drift_torch_(q, k, v, wl, layer, s, heads)
+    dt = storage_dtype_torch(wl)
+    return tuple(t.to(dt) for t in (q, k, v))

@@ -47,12 +47,85 @@ class Event:
         self.time = None
 
 
+class LazyFuture:
+    def __init__(self, ex, fn):
+        self.ex, self.fn, self.done, self.value = ex, fn, False, None
+
+    def result(self):
+        self.ex.run_until(self)
+        return self.value
+
+
+class LazyExecutor:
+    """One worker, submission order, but a job runs only when some thread needs its
+    result (or a later job's): the compute thread must never use an event before
+    the job that records it has run."""
+
+    def __init__(self):
+        self.queue = []
+
+    def submit(self, fn):
+        f = LazyFuture(self, fn)
+        self.queue.append(f)
+        return f
+
+    def run_until(self, f):
+        while not f.done:
+            g = self.queue.pop(0)
+            g.value = g.fn()
+            g.done = True
+
+
+class HostChunk:
+    def __init__(self, name, size):
+        self.name, self.size, self.views = name, size, []
+
+
 class FakeBackend:
-    def __init__(self, seed):
+    def __init__(self, seed, pinned_ok=True):
         self.rng = random.Random(seed)
         self.compute = Stream("compute")
         self.side = Stream("side")
         self.n = 0
+        self.ex = LazyExecutor()
+        self.chunks = []
+        self.pageable = []
+        self.pinned_ok = pinned_ok
+
+    def submit(self, fn):
+        return self.ex.submit(fn)
+
+    def nbytes(self, shape, dtype):
+        return 1000  # every tensor of an entry: 1,000 bytes
+
+    def empty_pageable(self, shape, dtype):
+        self.n += 1
+        b = Buf(f"host{self.n}")
+        self.pageable.append(b)
+        return b
+
+    def empty_pinned_bytes(self, nbytes):
+        assert self.pinned_ok, "pinned memory requested with a zero budget"
+        assert nbytes & (nbytes - 1) == 0, "pinned chunks must be powers of two"
+        self.n += 1
+        c = HostChunk(f"chunk{self.n}", nbytes)
+        self.chunks.append(c)
+        return c
+
+    def host_size(self, buf):
+        return buf.size
+
+    def host_view(self, buf, offset, nbytes):
+        if isinstance(buf, HostChunk):
+            assert 0 <= offset and offset + nbytes <= buf.size
+            assert all(offset + nbytes <= o or o + n <= offset for o, n, _ in buf.views), "overlapping views"
+            v = Buf(f"{buf.name}[{offset}:{offset + nbytes}]")
+            buf.views.append((offset, nbytes, v))
+            return v
+        return Buf(f"{buf.name}.{offset}")  # sub-view of a view: the entry's tensors
+
+    def typed(self, raw, shape, dtype):
+        return raw
 
     def compute_stream(self):
         return self.compute
@@ -118,6 +191,7 @@ def replay(cache, be, layers, steps, warmup=2, interval=3):
             nxt_step, nxt_layer = (step, layer + 1) if layer + 1 < layers else (step + 1, 0)
             if nxt_step < steps and step_kind(nxt_step, warmup, interval) == "reuse":
                 cache.prefetch(nxt_layer, busy_layer=layer)
+    cache.drain()  # run the side-stream jobs nobody waited for (their copies are checked too)
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -193,7 +267,7 @@ def test_mixed_residency_orders_every_access_and_copies_only_offloaded_layers(se
     anchors = sum(1 for s in range(steps) if step_kind(s, warmup, interval) == "anchor")
     offloaded = layers - resident
     # every device -> host copy is of an offloaded layer, once per anchor and tensor
-    assert cache.bytes_d2h == anchors * offloaded * len(SHAPES)
+    assert cache.bytes_d2h == anchors * offloaded * len(SHAPES) * 1000
     assert all((k == MCS_COPY_D2H) == (d in host_names) for d, _, k in copied)
     if offloaded == 0:
         assert copied == []
@@ -214,3 +288,51 @@ def test_entry_bytes_of_the_trajectory_layer():
     # perm 11.4 MB + lists 3.18 GB + residual 730 MB; with bitmaps 1.40 GB
     assert entry_bytes(wl, 0.15, False) == 24 * (4 * 118800 + 4 * 1857 * 17824 + 118800 * 128 * 2)
     assert entry_bytes(wl, 0.15, True) == 1403235936
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("budget_entries", [0, 1, 3, 100])
+def test_pinned_budget_splits_host_copies_and_orders_every_access(seed, budget_entries):
+    # one entry = 3 tensors of 1,000 bytes, padded to 3 x 1,024; chunks of 4,096 bytes
+    # hold one entry each (two would need 6,144)
+    be = FakeBackend(seed, pinned_ok=budget_entries > 0)
+    layers = 6
+    cache = MetaCache(layers, SHAPES, be, offload=True, device_slots=2, pinned_budget=4096 * budget_entries,
+                      pinned_chunk=4096)
+    pinned = [l for l in range(layers) if cache.entries[l].pinned]
+    assert pinned == list(range(min(budget_entries, layers)))
+    assert cache.arena.reserved <= 4096 * budget_entries
+    assert all(c.size == 4096 for c in be.chunks)
+    assert cache.host_pinned_bytes == 3000 * len(pinned)
+    assert cache.host_pageable_bytes == 3000 * (layers - len(pinned))
+    assert len(be.pageable) == 3 * (layers - len(pinned))
+    replay(cache, be, layers, steps=12)
+    assert cache.bytes_h2d > 0
+
+
+def test_pinned_chunks_pack_several_entries():
+    be = FakeBackend(0)
+    cache = MetaCache(8, SHAPES, be, offload=True, device_slots=2, pinned_budget=1 << 20, pinned_chunk=1 << 15)
+    # all eight entries (3 x 1,024 bytes each) fit one chunk (views checked for overlap)
+    assert len(be.chunks) == 1 and be.chunks[0].size == 1 << 15
+    assert len(be.chunks[0].views) == 8
+    assert all(e.pinned for e in cache.entries)
+
+
+def test_lazy_worker_is_needed_by_the_protocol():
+    # a compute-thread wait on an event whose job never ran is caught by the fake
+    be = FakeBackend(1)
+    cache = MetaCache(4, SHAPES, be, offload=True, device_slots=2)
+    real_await = cache._await
+    cache._await = lambda fut: None if fut is None else (fut.value if fut.done else be.event())
+    with pytest.raises(AssertionError, match="never recorded"):
+        replay(cache, be, 4, steps=12)
+    cache._await = real_await
+
+
+def test_bad_pinned_arguments():
+    be = FakeBackend(0)
+    with pytest.raises(ValueError):
+        MetaCache(3, SHAPES, be, offload=True, pinned_budget=-1)
+    with pytest.raises(ValueError):
+        MetaCache(3, SHAPES, be, offload=True, pinned_chunk=3000)

@@ -183,3 +183,41 @@ def test_select_on_one_query_per_group_is_per_query_topk(dtype, d, n, k):
         assert_close(host(o)[h][toks[h]], want, mx, mn, f"per-query attention h{h}")
         cap = ref.captured_mass(q[h][toks[h]], kk[h], keys, scale, lse_full[toks[h]])
         assert_close(np.exp(host(lse)[h][toks[h]] - lse_full[toks[h]]), cap, 5e-4, 5e-5, f"per-query mass h{h}")
+
+
+def test_drift_study_figures_match_the_oracle():
+    # drift.run's per-step figures on the tiny fp32 workload against the same
+    # quantities from the fp64 oracle, on the same inputs (the generator's steps)
+    # and the GPU anchor's groups and kept keys: reuse and no-residual errors
+    # against fresh dense attention, and how far the residual and the output move.
+    import torch as _t
+
+    from sparse_attention_diffusion_amd import drift
+    wl = W.WORKLOADS["tiny"]
+    cap = {}
+    res = drift.run("tiny", density=0.2, steps=3, drift=0.05, reps=1, capture=cap)
+    kk = wl.topk(0.2)
+    perm = host(cap["perm"])[0]
+    idx = host(cap["idx"])[0][:, :kk]
+    s = 1.0 / np.sqrt(wl.head_dim)
+    dev_ = _t.device("cuda:0")
+
+    def inputs(step):
+        return tuple(host(t)[0] for t in W.make_qkv_torch(wl, dev_, step=step))
+
+    q0, k0, v0 = inputs(0)
+    o0 = ref.dense_attention(q0, k0, v0, s)
+    r0 = o0 - ref.sparse_attention(q0, k0, v0, perm, idx, 64, s)
+    for row in res["steps"]:
+        qt, kt, vt = inputs(row["step"])
+        ot = ref.dense_attention(qt, kt, vt, s)
+        st = ref.sparse_attention(qt, kt, vt, perm, idx, 64, s)
+        want = {"reuse_mean_abs": np.abs(st + r0 - ot).mean(), "no_residual_mean_abs": np.abs(st - ot).mean(),
+                "resid_change_rel": np.linalg.norm((ot - st) - r0) / np.linalg.norm(r0),
+                "output_change_rel": np.linalg.norm(ot - o0) / np.linalg.norm(o0)}
+        decimals = {"reuse_mean_abs": 6, "no_residual_mean_abs": 6, "resid_change_rel": 5, "output_change_rel": 5}
+        for key, w in want.items():
+            # fp32 kernels against fp64: 1e-5 absolute on these O(1e-3 .. 1e-1) figures,
+            # plus the rounding of the reported value
+            assert abs(row[key] - w) <= 1e-5 + 0.5 * 10.0 ** -decimals[key], (row["step"], key, row[key], w)
+        print(f"step {row['step']}: " + ", ".join(f"{k} {row[k]:.5g} (oracle {w:.5g})" for k, w in want.items()))

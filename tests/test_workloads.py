@@ -62,3 +62,18 @@ def test_pct_of_ideal_reproduces_the_pages_kernel_speed_figure():
     assert abs(got - 0.958) < 1e-12
     assert round(got, 2) == fig["fraction_of_ideal"]
     assert W.WORKLOADS["wan14b_720p"].n == fig["tokens"]
+
+
+def test_schedule_cost_closed_forms():
+    # the trajectory's own schedule (5 dense steps, anchors every 5 of 50) with unit
+    # dense cost, anchor = 2 and reuse = density: 5 + 9 * 2 + 36 * 0.15 = 28.4
+    from sparse_attention_diffusion_amd.drift import schedule_cost
+    sp, ov = schedule_cost(1.0, 2.0, 0.15, 50, 5, 5, 0.15)
+    assert abs(sp - 50 / 28.4) < 1e-12
+    assert abs(ov - (28.4 - 5 - 45 * 0.15) / 45 * 100) < 1e-9
+    # an anchor that costs no more than a reuse step adds nothing over the density
+    sp, ov = schedule_cost(1.0, 0.2, 0.2, 50, 0, 7, 0.2)
+    assert abs(ov) < 1e-9 and abs(sp - 5.0) < 1e-12
+    # gap 1: every sparse step is an anchor
+    sp, ov = schedule_cost(1.0, 3.0, 0.1, 10, 2, 1, 0.1)
+    assert abs(sp - 10 / (2 + 8 * 3.0)) < 1e-12
