@@ -148,7 +148,13 @@ int mcs_sparse_attn(const mcs_dims* d, const void* q, const void* k, const void*
  * dense attention (with its logsumexp); idx = top-K selection on perm reusing
  * the dense pass's row statistics; resid = o_dense - sparse attention(perm,
  * idx).  The anchor's attention output is o_dense.  lse may be NULL.  Needs
- * workspace (op ANCHOR). */
+ * workspace: with at least the op ANCHOR figure for heads_per_pass 1 (the
+ * grouping's and the selection's regions side by side), grouping runs on a
+ * library-owned side stream of the current device (default priority, created on
+ * first use, kept until the process ends) beside dense attention, forked from
+ * and joined back into `stream` with events before selection; with less, but
+ * at least max(op GROUP, op SELECT with heads_per_pass 1), the steps run in
+ * turn on `stream`.  Both give the same bits. */
 int mcs_anchor(const mcs_dims* d, const void* q, const void* k, const void* v, int32_t* perm, int32_t* idx,
                void* resid, void* o_dense, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 

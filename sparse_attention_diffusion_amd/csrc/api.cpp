@@ -74,6 +74,9 @@ int mass_ld(const mcs_dims* d) { return (d->n + 3) & ~3; }
 size_t mass_bytes_per_head(const mcs_dims* d) { return align256((size_t)groups_of(d) * mass_ld(d) * 4); }
 size_t group_ws(const mcs_dims* d) { return mcs::pddp_workspace_bytes(d->heads, d->n, d->head_dim, d->group); }
 size_t select_ws(const mcs_dims* d, int hpp) { return stats_bytes(d) + (size_t)hpp * mass_bytes_per_head(d); }
+// The anchor keeps the grouping's workspace beside the selection's, so that
+// grouping can run while dense attention writes the row statistics.
+size_t anchor_ws(const mcs_dims* d, int hpp) { return align256(group_ws(d)) + select_ws(d, hpp); }
 
 mcs::AttnArgs attn_args(const mcs_dims* d, const void* q, const void* k, const void* v) {
   mcs::AttnArgs a{};
@@ -155,6 +158,28 @@ int scratch_address(void** out) {
   return MCS_OK;
 }
 
+// One stream per device for work that runs beside the caller's stream inside
+// a call (grouping beside dense attention in mcs_anchor).  Created on first
+// use with the default priority; it lives until the process ends.
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxDevices] = {};
+
+int side_stream(hipStream_t* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MCS_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (!g_side[dev]) {
+    hipStream_t s = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+    g_side[dev] = s;
+  }
+  *out = g_side[dev];
+  return MCS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,11 +197,7 @@ int mcs_workspace_bytes(const mcs_dims* d, int32_t op, int32_t hpp, size_t* byte
   switch (op) {
     case MCS_OP_GROUP: *bytes = group_ws(d); return MCS_OK;
     case MCS_OP_SELECT: *bytes = select_ws(d, h); return MCS_OK;
-    case MCS_OP_ANCHOR: {
-      const size_t a = group_ws(d), b = select_ws(d, h);
-      *bytes = a > b ? a : b;
-      return MCS_OK;
-    }
+    case MCS_OP_ANCHOR: *bytes = anchor_ws(d, h); return MCS_OK;
     case MCS_OP_BLOCK_SELECT: *bytes = align256(mcs::block_select_ws_bytes(d->heads, d->n, d->head_dim)); return MCS_OK;
     default: return fail(MCS_EINVAL, "unknown op %d", op);
   }
@@ -296,21 +317,51 @@ int mcs_anchor(const mcs_dims* d, const void* q, const void* k, const void* v, i
   if (lse) CHECK(check_ptr(lse, 4, "lse"));
   CHECK(check_ptr(ws, 256, "workspace"));
   if (ws_bytes < group_ws(d)) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, group_ws(d));
-  const int hpp = heads_per_pass(d, ws_bytes);
+  // With room for both workspaces, grouping runs on a side stream beside dense
+  // attention (they share only q); otherwise one after the other.
+  const bool overlap = ws_bytes >= anchor_ws(d, 1);
+  const size_t sel_off = overlap ? align256(group_ws(d)) : 0;
+  const int hpp = heads_per_pass(d, ws_bytes - sel_off);
   if (hpp < 1) return fail(MCS_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, select_ws(d, 1));
-  // 1. grouping
+  char* sel_ws = (char*)ws + sel_off;
   mcs::PddpArgs pa{q, perm, ws, d->heads, d->n, d->head_dim, d->group, d->power_iters};
-  hipError_t e = mcs::launch_pddp(pa, d->dtype, stream);
-  if (e != hipSuccess) return hip_fail(e, "pddp launch");
   // 2. dense attention; its row statistics double as selection pass 1
-  float2* stats = (float2*)ws;
-  float* mass = (float*)((char*)ws + stats_bytes(d));
+  float2* stats = (float2*)sel_ws;
+  float* mass = (float*)(sel_ws + stats_bytes(d));
   mcs::AttnArgs a = attn_args(d, q, k, v);
   a.o = o_dense;
   a.lse = lse;
   a.stats = stats;
-  e = mcs::launch_attention(a, d->dtype, d->head_dim, false, mcs::EPI_PLAIN, true, stream);
-  if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  hipError_t e;
+  if (overlap) {
+    hipStream_t side = nullptr;
+    CHECK(side_stream(&side));
+    hipEvent_t fork = nullptr, join = nullptr;
+    if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) != hipSuccess) {
+      hipEventDestroy(fork);
+      return hip_fail(e, "hipEventCreate");
+    }
+    // 1. grouping on the side stream, after everything queued on `stream` so far
+    hipError_t eg = hipEventRecord(fork, stream);
+    if (eg == hipSuccess) eg = hipStreamWaitEvent(side, fork, 0);
+    if (eg == hipSuccess) eg = mcs::launch_pddp(pa, d->dtype, side);
+    const hipError_t ed = mcs::launch_attention(a, d->dtype, d->head_dim, false, mcs::EPI_PLAIN, true, stream);
+    // join before anything else is queued on `stream`, whatever failed
+    hipError_t ej = hipEventRecord(join, side);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, join, 0);
+    hipEventDestroy(fork);
+    hipEventDestroy(join);
+    if (eg != hipSuccess) return hip_fail(eg, "pddp launch on the side stream");
+    if (ed != hipSuccess) return hip_fail(ed, "dense attention launch");
+    if (ej != hipSuccess) return hip_fail(ej, "side stream join");
+  } else {
+    // 1. grouping
+    e = mcs::launch_pddp(pa, d->dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "pddp launch");
+    e = mcs::launch_attention(a, d->dtype, d->head_dim, false, mcs::EPI_PLAIN, true, stream);
+    if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  }
   // 3. selection pass 2 and top-K
   CHECK(run_select(d, q, k, perm, stats, nullptr, idx, mass, hpp, stream));
   // 4. residual = dense - sparse

@@ -108,3 +108,28 @@ def test_wan13b_480p_anchor_sampled_against_oracle():
         assert_close(host(out["o_dense"])[hi][rows], o_dense, what="o_dense sampled")
         o_sp = ref.sparse_attention(q[hi], k[hi], v[hi], perm, {g: idx[g][:kk] for g in groups}, 64, s, groups=groups)
         assert_close(host(out["resid"])[hi][rows], o_dense - o_sp[rows], what="resid sampled")
+
+
+def test_anchor_with_grouping_beside_dense_equals_serial_anchor():
+    """A workspace holding both the grouping and the selection regions lets the
+    anchor group on a side stream while dense attention runs; one of
+    max(group, select) bytes runs the steps in turn.  Both give the same bits,
+    also when anchors follow each other with no host synchronisation between."""
+    wl = W.Workload("t", (7, 11, 19), 5, 128, "bf16", 64, (0.2,), 11, 0.0, 0)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_dev(x, wl.dtype) for x in (q, k, v))
+    kk = wl.topk(0.2)
+    d = mcs.make_dims(qd, topk=kk)
+    n_group = mcs.mcs_workspace_bytes(d, mcs.MCS_OP_GROUP)
+    n_select = mcs.mcs_workspace_bytes(d, mcs.MCS_OP_SELECT)
+    n_anchor = mcs.mcs_workspace_bytes(d, mcs.MCS_OP_ANCHOR)
+    assert n_anchor >= n_group + n_select
+    ws_serial = torch.empty(max(n_group, n_select), dtype=torch.uint8, device=qd.device)
+    ws_side = torch.empty(n_anchor, dtype=torch.uint8, device=qd.device)
+    serial = mcs.mcs_anchor(qd, kd, vd, kk, want_lse=True, ws=ws_serial)
+    side = [mcs.mcs_anchor(qd, kd, vd, kk, want_lse=True, ws=ws_side) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert ref.pddp_verify(q[0], host(serial["perm"])[0], 64)["bad"] == 0
+    for out in side:
+        for key in ("perm", "idx", "resid", "o_dense", "lse"):
+            assert torch.equal(out[key], serial[key]), key
