@@ -71,7 +71,11 @@ int check_ptr(const void* p, size_t align, const char* name) {
 
 size_t stats_bytes(const mcs_dims* d) { return align256((size_t)d->heads * d->n * 8); }
 int mass_ld(const mcs_dims* d) { return (d->n + 3) & ~3; }
-size_t mass_bytes_per_head(const mcs_dims* d) { return align256((size_t)groups_of(d) * mass_ld(d) * 4); }
+size_t mass_rows_bytes_per_head(const mcs_dims* d) { return align256((size_t)groups_of(d) * mass_ld(d) * 4); }
+constexpr size_t kHistBytesPerGroup = 4096 * 4;  // a mass row's 12-bit histogram
+size_t mass_bytes_per_head(const mcs_dims* d) {
+  return mass_rows_bytes_per_head(d) + align256((size_t)groups_of(d) * kHistBytesPerGroup);
+}
 size_t group_ws(const mcs_dims* d) { return mcs::pddp_workspace_bytes(d->heads, d->n, d->head_dim, d->group); }
 size_t select_ws(const mcs_dims* d, int hpp) { return stats_bytes(d) + (size_t)hpp * mass_bytes_per_head(d); }
 // The anchor keeps the grouping's workspace beside the selection's, so that
@@ -106,6 +110,8 @@ int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
     m.stats = stats;
     m.lse = lse;
     m.mass = mass;
+    // the histograms follow the mass rows of hpp heads
+    m.hist = (uint32_t*)((char*)mass + (size_t)hpp * mass_rows_bytes_per_head(d));
     m.ldm = mass_ld(d);
     m.h0 = h0;
     m.hcount = hc;

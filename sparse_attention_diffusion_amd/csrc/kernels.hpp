@@ -54,6 +54,7 @@ struct MassArgs {
   const float2* stats;     // [H][N] row statistics from pass 1 (or null: use lse)
   const float* lse;        // [H][N] natural-log logsumexp (used when stats is null)
   float* mass;             // [hcount][G][ldm] scratch rows
+  uint32_t* hist;          // [hcount][G][4096] scratch: each row's histogram of its top 12 value bits
   int ldm;                 // row stride of mass: N rounded up to a multiple of 4
   int32_t* idx;            // [H][G][kpad] output
   int h0, hcount, N, G, K, kpad;

@@ -8,12 +8,17 @@
 // all keys, 32 at a time (v_mfma_f32_32x32x16_bf16 with the group's queries as
 // the A operand, so each lane owns one key column), normalises each logit with
 // its row statistics and sums the 64 probabilities per key: mass[g][j].
-// Top-K, fused into the same wavefront: while the row is produced a 4096-bin
-// histogram of its top 12 value bits is built in LDS (non-negative floats order
-// like their bit patterns); afterwards the wave finds the bin of the K-th largest
-// mass, gathers that bin's entries, resolves the exact threshold among them and
-// writes the kept key ids in ascending order, ties at the threshold going to the
-// lowest ids.  The row is re-read while it is still in cache.
+// While the row is produced, a 4096-bin histogram of its top 12 value bits is
+// built in LDS (non-negative floats order like their bit patterns) and stored
+// beside the row when the loop ends.
+// Top-K (a second kernel, four waves per SIMD so that the row reads overlap):
+// one wavefront per row finds the bin of the K-th largest mass from the stored
+// histogram, then reads the row once.  Every entry above that bin, and every
+// entry in it (a candidate, flagged), goes to a provisional ascending list that
+// overwrites the row's head, while the candidates' values go to LDS.  The exact
+// threshold is resolved among the candidates, and a pass over the provisional
+// list (about K entries, not N) writes the kept key ids in ascending order, ties
+// at the threshold going to the lowest ids.
 #include <type_traits>
 
 #include "common.hpp"
@@ -34,14 +39,15 @@ struct QTile {
   __device__ static uint32_t khalf_off(int hf) { return F32 ? (uint32_t)(D / 2 * 4 * hf) : (uint32_t)(16 * hf); }
 };
 
-// Per-wave shared memory of the fused top-K: a 4096-bin histogram of the top 12
-// value bits, and a candidate list (bit pattern, key id) of the histogram bin that
-// holds the K-th largest mass.
+// The loop's histogram: 4096 bins of the top 12 value bits (30..19) of a mass.
 constexpr int kHistBins = 4096;
+// Per-wave shared memory of the top-K: a 256-bin histogram for refining the
+// threshold, and the values of the candidates (entries of the threshold's bin),
+// in ascending key order.
 constexpr int kCandCap = 2048;
-struct WaveCand {
+struct WaveTopk {
+  uint32_t hist[256];
   uint32_t cand_bits[kCandCap];
-  int32_t cand_id[kCandCap];
 };
 
 // LDS atomic add issued through inline asm.  The compiler cannot tell LDS that a
@@ -110,7 +116,8 @@ __device__ uint32_t pick_digit(const uint32_t* hist, int bins, uint32_t& kr, uin
   return (uint32_t)d;
 }
 
-constexpr int kUnroll = 8;
+constexpr int kMassStages = 6;  // K tiles in flight in the bf16 pass-2 loop
+constexpr int kUnroll = 4;
 constexpr int kBatch = 256 * kUnroll;
 
 // Entries [base, base + kBatch) of a row: lane l gets entries base + 256*u + 4*l + j.
@@ -131,8 +138,9 @@ __device__ __forceinline__ void load_batch(const uint32_t* rb, int N, int base, 
 }
 
 // Visit a row in batches of kBatch entries, the loads of batch n+1 in flight
-// while batch n is processed (the scan is bound by load latency, not by the
-// per-entry work).  f(base, b) sees entries base + 256*u + 4*lane + j.
+// while batch n is processed.  f(base, b) sees entries base + 256*u + 4*lane + j.
+// (Latency is hidden mostly by the other waves of the SIMD: the top-K kernel
+// runs four per SIMD.)
 template <typename F>
 __device__ __forceinline__ void scan_row(const uint32_t* rb, int N, F&& f) {
   uint32_t ba[kUnroll][4], bb[kUnroll][4];
@@ -147,23 +155,58 @@ __device__ __forceinline__ void scan_row(const uint32_t* rb, int N, F&& f) {
   if (base < N) f(base, ba);
 }
 
-// Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
-// id.  `hist` already holds the 12-bit histogram (bits 30..19) of the row.
-__device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out, uint32_t* hist, WaveCand* w) {
+// Bin (from the top) of a stored 4096-bin histogram that holds the kr-th
+// largest entry (1-based); leaves in kr the rank inside that bin and in cnt its
+// population.  Lane l sums bins [64l, 64l + 64); suffix sums over the lanes find
+// the lane, then over that lane's 64 bins the bin.
+__device__ uint32_t pick_top_bin(const uint32_t* gh, uint32_t& kr, uint32_t& cnt) {
   const int lane = threadIdx.x & 63;
-  const uint32_t* rb = reinterpret_cast<const uint32_t*>(row);
+  auto suffix = [&](uint32_t x) {  // inclusive: sum over lanes >= this one
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_down((int)x, o, 64);
+      if (lane + o < 64) x += y;
+    }
+    return x;
+  };
+  const u32x4* p = reinterpret_cast<const u32x4*>(gh + 64 * lane);
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const u32x4 v = p[i];
+    t += v[0] + v[1] + v[2] + v[3];
+  }
+  uint32_t inc = suffix(t);
+  // exactly one lane has inc >= kr > inc - t (the histogram holds N >= K entries)
+  uint64_t m = __builtin_amdgcn_ballot_w64(inc >= kr && inc - t < kr);
+  const int L = m ? __builtin_ctzll(m) : 0;
+  uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(inc - t), L);
+  const uint32_t c = gh[64 * L + lane];
+  inc = suffix(c) + above;
+  m = __builtin_amdgcn_ballot_w64(inc >= kr && inc - c < kr);
+  const int j = m ? __builtin_ctzll(m) : 0;
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+  kr -= (uint32_t)__builtin_amdgcn_readlane((int)(inc - c), j);
+  return (uint32_t)(64 * L + j);
+}
+
+// Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
+// id.  gh is the row's stored 12-bit histogram.  The row's head is overwritten
+// by the provisional list.
+__device__ void wave_topk(float* row, const uint32_t* gh, int N, int K, int kpad, int32_t* out, WaveTopk* w) {
+  const int lane = threadIdx.x & 63;
+  uint32_t* rb = reinterpret_cast<uint32_t*>(row);
   uint32_t kr = (uint32_t)K, cnt = 0;
-  uint32_t prefix = pick_digit(hist, kHistBins, kr, cnt) << 19;
+  uint32_t prefix = pick_top_bin(gh, kr, cnt) << 19;
   uint32_t pmask = 0xfffu << 19;
   int shift = 19;
-  // Refine the prefix while too many entries share it: bits 18..7, then 6..0.
-  // (Common when the masses near the threshold are dense: a 12-bit bin then holds
-  // thousands of entries.)  The row is read in the same batches as below.
+  // Refine the prefix while too many entries share it, 8 bits per pass (common
+  // when the masses near the threshold are dense: a 12-bit bin then holds
+  // thousands of entries).  The row is read in the same batches as below.
   while (cnt > (uint32_t)kCandCap && shift > 0) {
-    const int nshift = shift >= 12 ? shift - 12 : 0;
+    const int nshift = shift >= 8 ? shift - 8 : 0;
     const int bins = 1 << (shift - nshift);
-    const int hb = bins < 64 ? 64 : bins;
-    for (int j = lane; j < hb; j += 64) hist[j] = 0;
+    for (int j = lane; j < 256; j += 64) w->hist[j] = 0;
     __builtin_amdgcn_s_waitcnt(0);
     scan_row(rb, N, [&](int base, const uint32_t (&b)[kUnroll][4]) {
 #pragma unroll
@@ -172,97 +215,138 @@ __device__ void wave_topk(const float* row, int N, int K, int kpad, int32_t* out
         for (int j = 0; j < 4; ++j) {
           const int i = base + 256 * u + 4 * lane + j;
           if (i < N && (b[u][j] & pmask) == prefix)
-            atomicAdd(&hist[(b[u][j] >> nshift) & (uint32_t)(bins - 1)], 1u);
+            atomicAdd(&w->hist[(b[u][j] >> nshift) & (uint32_t)(bins - 1)], 1u);
         }
     });
     __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t d = pick_digit(hist, hb, kr, cnt);
+    const uint32_t d = pick_digit(w->hist, 256, kr, cnt);
     prefix |= d << nshift;
     pmask |= (uint32_t)(bins - 1) << nshift;
     shift = nshift;
   }
-  // Candidates: entries matching the prefix, in ascending id order.  The row is
-  // read in batches of 8 x 256 entries (8 independent 16-byte loads per lane).
-  uint32_t nc = 0;
+  // One pass over the row: entries whose masked bits exceed the prefix are kept
+  // for sure, entries equal to it are candidates.  Both go, in id order, to the
+  // provisional list at the row's head (id, bit 31 set for a candidate); the
+  // candidates' values go to LDS.  The list position of an entry never exceeds
+  // its own index, and the batch read ahead lies past the current one, so no
+  // store lands on an entry not yet read.
+  uint32_t nsel = 0, nc = 0;
   scan_row(rb, N, [&](int base, const uint32_t (&b)[kUnroll][4]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i0 = base + 256 * u + 4 * lane;
-      bool f[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f[j] = i0 + j < N && (b[u][j] & pmask) == prefix;
-      uint32_t rank[4];
-      const uint32_t tot = flag_ranks(f, rank);
+      bool sel[4], cand[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t pos = nc + rank[j];
-        if (f[j] && pos < (uint32_t)kCandCap) {
-          w->cand_bits[pos] = b[u][j];
-          w->cand_id[pos] = i0 + j;
-        }
+        const uint32_t mb = b[u][j] & pmask;
+        sel[j] = i0 + j < N && mb >= prefix;
+        cand[j] = i0 + j < N && mb == prefix;
       }
-      nc += tot;
+      uint32_t rs[4], rc[4];
+      const uint32_t ts = flag_ranks(sel, rs);
+      const uint32_t tc = flag_ranks(cand, rc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (sel[j]) rb[nsel + rs[j]] = (uint32_t)(i0 + j) | (cand[j] ? 0x80000000u : 0u);
+        if (cand[j] && nc + rc[j] < (uint32_t)kCandCap) w->cand_bits[nc + rc[j]] = b[u][j];
+      }
+      nsel += ts;
+      nc += tc;
     }
   });
   if (nc > (uint32_t)kCandCap) nc = kCandCap;  // the refinement above keeps nc within the cap
+  // The list's stores have landed in L2, and this CU's L1 (which holds the row
+  // lines just read) is invalidated, before the list is read back.
   __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // Resolve the remaining low bits among the candidates, 8 at a time.
   while (shift > 0) {
     const int nshift = shift >= 8 ? shift - 8 : 0;
     const int bins = 1 << (shift - nshift);
-    for (int j = lane; j < 256; j += 64) hist[j] = 0;
+    for (int j = lane; j < 256; j += 64) w->hist[j] = 0;
     __builtin_amdgcn_s_waitcnt(0);
     for (uint32_t c = lane; c < nc; c += 64) {
       const uint32_t b = w->cand_bits[c];
-      if ((b & pmask) == prefix) atomicAdd(&hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
+      if ((b & pmask) == prefix) atomicAdd(&w->hist[(b >> nshift) & (uint32_t)(bins - 1)], 1u);
     }
     __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t d = pick_digit(hist, 256, kr, cnt);
+    const uint32_t d = pick_digit(w->hist, 256, kr, cnt);
     prefix |= d << nshift;
     pmask |= (uint32_t)(bins - 1) << nshift;
     shift = nshift;
   }
   const uint32_t tau = prefix;  // the K-th largest bit pattern; keep kr of its ties
-  // Ascending compaction, same batching: 4 consecutive entries per lane.
-  // The kept ids go out through a buffer descriptor covering exactly K entries,
-  // one store instruction per (u, j) whatever is kept (the rest aim past the
-  // range and are dropped): with a fixed number of stores per batch the
-  // compiler's wait for the next batch's loads need not cover them.
+  // Ascending compaction of the provisional list: sure entries are kept; a
+  // candidate (the c-th, in id order) is kept if its value exceeds tau, or equals
+  // it and is among the first kr such.  The kept ids go out through a buffer
+  // descriptor covering exactly K entries, one store instruction per (u, j)
+  // whatever is kept (the rest aim past the range and are dropped).
   const auto rout = make_rsrc(out, (uint32_t)K * 4u);
-  uint32_t written = 0, eq_seen = 0;
-  scan_row(rb, N, [&](int base, const uint32_t (&bb)[kUnroll][4]) {
+  uint32_t written = 0, eq_seen = 0, cand_seen = 0;
+  scan_row(rb, (int)nsel, [&](int base, const uint32_t (&bb)[kUnroll][4]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i0 = base + 256 * u + 4 * lane;
-      const uint32_t* b = bb[u];
-      // entries above tau are kept; of those equal to tau, the first kr in id order
-      bool eq[4], keep[4];
+      bool isc[4], eq[4], keep[4];
+      uint32_t cb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) eq[j] = i0 + j < N && b[j] == tau;
+      for (int j = 0; j < 4; ++j) isc[j] = i0 + j < (int)nsel && (bb[u][j] >> 31) != 0;
+      uint32_t crank[4];
+      const uint32_t ctot = flag_ranks(isc, crank);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // a candidate past the LDS cap exists only when the refinement ran down
+        // to the last bit (more than kCandCap entries share one value): it equals tau
+        const uint32_t ci = cand_seen + crank[j];
+        cb[j] = isc[j] ? (ci < nc ? w->cand_bits[ci] : tau) : 0u;
+        eq[j] = isc[j] && cb[j] == tau;
+      }
       uint32_t eq_rank[4];
       const uint32_t eq_tot = flag_ranks(eq, eq_rank);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) keep[j] = (i0 + j < N && b[j] > tau) || (eq[j] && eq_seen + eq_rank[j] < kr);
+      for (int j = 0; j < 4; ++j)
+        keep[j] = i0 + j < (int)nsel && (!isc[j] || cb[j] > tau || (eq[j] && eq_seen + eq_rank[j] < kr));
       uint32_t rank[4];
       const uint32_t sel_tot = flag_ranks(keep, rank);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t off = keep[j] ? (written + rank[j]) * 4u : 0xfffffff0u;  // exactly K are kept overall
         asm volatile("" : "+v"(off));  // opaque: keeps the store out of a branch on keep[j]
-        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(i0 + j), rout, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(bb[u][j] & 0x7fffffffu, rout, off, 0, 0);
       }
       written += sel_tot;
       eq_seen += eq_tot;
+      cand_seen += ctot;
     }
   });
   for (int j = K + lane; j < kpad; j += 64) out[j] = -1;
+}
+
+// Top-K of rows [0, hcount*G) of a pass: one wavefront per row, four per SIMD.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void topk_rows_kernel(MassArgs a) {
+  __shared__ WaveTopk s_w[4];
+  const int wid = wave_id();
+  const int item = blockIdx.x * 4 + wid;
+  if (item >= a.hcount * a.G) return;  // no block-level synchronisation below
+  const int hl = item / a.G, g = item - hl * a.G;
+  wave_topk(a.mass + (size_t)item * a.ldm, a.hist + (size_t)item * kHistBins, a.N, a.K, a.kpad,
+            a.idx + ((size_t)(a.h0 + hl) * a.G + g) * a.kpad, &s_w[wid]);
+}
+
+// Store a wave's LDS histogram to its row's slot: 16 consecutive bytes per lane.
+__device__ __forceinline__ void store_hist(const uint32_t* hist, uint32_t* gh) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kHistBins / 256; ++i) {
+    const int e = 4 * (64 * i + lane);
+    *reinterpret_cast<u32x4*>(gh + e) = *reinterpret_cast<const u32x4*>(hist + e);
+  }
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   using TL = QTile<T, D>;
   __shared__ uint32_t s_hist[4][kHistBins];
-  extern __shared__ WaveCand wcand[];
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int hf = lane >> 5, lm = lane & 31;
   const int items = a.hcount * a.G;
@@ -270,7 +354,6 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   if (blk < 0) return;
   const int item = blk * 4 + wid;
   if (item >= items) return;  // no block-level synchronisation below
-  WaveCand* w = &wcand[wid];
   uint32_t* hist = s_hist[wid];
   const int hl = item / a.G, g = item - hl * a.G;
   const int h = a.h0 + hl;
@@ -386,11 +469,8 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
   } else {
     reduce_store(sa, it * 32);
   }
-  // The row is complete once this wave's stores have landed; its L1 lines were
-  // never read before, so loads issued after the wait see the stored values.
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, hist, w);
+  __builtin_amdgcn_s_waitcnt(0);  // the histogram's LDS atomics are done
+  store_hist(hist, a.hist + (size_t)item * kHistBins);
 }
 
 // bf16 pass 2 with K staged through LDS.  Every group scans all keys in the
@@ -402,9 +482,8 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
 //
 // With one block per CU, the copies in flight set the pace: two 8 KiB stages
 // held the loop at about 4 TB/s of K, at the copy latency, whatever the math.
-// So the tiles rotate through NS = 6 stages, copied NS steps ahead: two stages
-// after the candidate areas, and one in each wave's top-K candidate area (free
-// until the loop ends).
+// So the tiles rotate through NS = 6 stages, copied NS steps ahead, after the
+// four waves' histograms.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void group_mass_lds_kernel(MassArgs a) {
@@ -419,14 +498,9 @@ void group_mass_lds_kernel(MassArgs a) {
   const int g = (blk - hl * gb) * 4 + wid;
   const bool active = g < a.G;  // a wave past the last group only helps copy
   uint32_t* hist = (uint32_t*)smem + wid * kHistBins;
-  WaveCand* w = (WaveCand*)(smem + 4 * kHistBins * sizeof(uint32_t)) + wid;
   LDSP char* lbase = (LDSP char*)smem + 4 * kHistBins * sizeof(uint32_t);
-  constexpr int NS = 6;
-  static_assert(sizeof(WaveCand) >= (size_t)L::TILE, "a K tile fits a candidate area");
-  // stage j: two after the candidate areas, then the candidate area of wave j - 2
-  auto stage = [&](int j) -> LDSP char* {
-    return lbase + (j < 2 ? 4 * (int)sizeof(WaveCand) + j * L::TILE : (j - 2) * (int)sizeof(WaveCand));
-  };
+  constexpr int NS = kMassStages;
+  auto stage = [&](int j) -> LDSP char* { return lbase + j * L::TILE; };
   const int h = a.h0 + hl;
   const int N = a.N;
   const size_t head_off = (size_t)h * N * L::ROWB;
@@ -551,20 +625,17 @@ void group_mass_lds_kernel(MassArgs a) {
   } else {
     reduce_store(sa, it * 32);
   }
-  // The copies past the last step land, and every wave is done with the stages,
-  // before the candidate areas are written (or the block's LDS is released).
+  // The copies past the last step land before the block's LDS is released.
   wait_vm<0>();
-  block_barrier();
-  if (!active) return;  // no block-level synchronisation below
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  wave_topk(out, N, a.K, a.kpad, a.idx + ((size_t)h * a.G + g) * a.kpad, hist, w);
+  if (!active) return;
+  __builtin_amdgcn_s_waitcnt(0);  // the histogram's LDS atomics are done
+  store_hist(hist, a.hist + ((size_t)hl * a.G + g) * kHistBins);
 }
 
 template <int D>
 hipError_t launch_mass_lds(const MassArgs& a, hipStream_t s) {
   const int blocks = xcd_grid(a.hcount * ((a.G + 3) / 4));
-  const size_t lds = 4 * (kHistBins * sizeof(uint32_t) + sizeof(WaveCand)) + 2 * LT<D>::TILE;
+  const size_t lds = 4 * kHistBins * sizeof(uint32_t) + kMassStages * LT<D>::TILE;
   hipError_t e = hipFuncSetAttribute((const void*)group_mass_lds_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -576,19 +647,22 @@ template <typename T, int D>
 hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   const int items = a.hcount * a.G;
   const int blocks = xcd_grid((items + 3) / 4);
-  const size_t lds = 4 * sizeof(WaveCand);  // + the static histograms
-  hipError_t e = hipFuncSetAttribute((const void*)group_mass_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((group_mass_kernel<T, D>), dim3(blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((group_mass_kernel<T, D>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s) {
-  if (dtype == DT_BF16) return head_dim == 128 ? launch_mass_lds<128>(a, s) : launch_mass_lds<64>(a, s);
-  return head_dim == 128 ? launch_mass_t<float, 128>(a, s) : launch_mass_t<float, 64>(a, s);
+  hipError_t e;
+  if (dtype == DT_BF16)
+    e = head_dim == 128 ? launch_mass_lds<128>(a, s) : launch_mass_lds<64>(a, s);
+  else
+    e = head_dim == 128 ? launch_mass_t<float, 128>(a, s) : launch_mass_t<float, 64>(a, s);
+  if (e != hipSuccess) return e;
+  const int rows = a.hcount * a.G;
+  hipLaunchKernelGGL(topk_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace mcs
