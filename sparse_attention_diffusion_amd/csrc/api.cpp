@@ -97,12 +97,15 @@ mcs::AttnArgs attn_args(const mcs_dims* d, const void* q, const void* k, const v
   return a;
 }
 
-// Pass 2 + top-K over head chunks; stats (from pass 1 or the dense pass) or lse.
+// Selection pass 2 and the top-K over all heads, hpp heads of mass rows at a
+// time: the loop writes the rows and their histograms, then the top-K reads
+// them.  (Running each pass's top-K on a second stream beside the next pass's
+// loop, with double-buffered rows, measured about 1 ms slower on the 40-head
+// benchmark layer: the top-K's memory traffic slows the loop more than it hides.)
 int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* perm, const float2* stats,
                const float* lse, int32_t* idx, float* mass, int hpp, hipStream_t s) {
   const int G = groups_of(d);
   for (int h0 = 0; h0 < d->heads; h0 += hpp) {
-    const int hc = d->heads - h0 < hpp ? d->heads - h0 : hpp;
     mcs::MassArgs m{};
     m.q = q;
     m.k = k;
@@ -114,7 +117,7 @@ int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
     m.hist = (uint32_t*)((char*)mass + (size_t)hpp * mass_rows_bytes_per_head(d));
     m.ldm = mass_ld(d);
     m.h0 = h0;
-    m.hcount = hc;
+    m.hcount = d->heads - h0 < hpp ? d->heads - h0 : hpp;
     m.N = d->n;
     m.G = G;
     m.c = (float)((double)d->scale * 1.4426950408889634);
@@ -124,6 +127,7 @@ int run_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
     m.kpad = d->kpad;
     hipError_t e = mcs::launch_group_mass(m, d->dtype, d->head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "selection pass 2 launch");
+    if ((e = mcs::launch_topk(m, s)) != hipSuccess) return hip_fail(e, "top-K launch");
   }
   return MCS_OK;
 }
@@ -263,8 +267,9 @@ int mcs_select_noalloc(const mcs_dims* d, const void* q, const void* k, const in
   void* ws = nullptr;
   CHECK(scratch_address(&ws));
   // Every byte the kernels read from the scratch is written earlier in the same
-  // call (row statistics by pass 1 for every token, each mass row by the wave
-  // that then reads it), so nothing left by an earlier call needs clearing.
+  // call (row statistics by pass 1 for every token, each mass row and its
+  // histogram by the pass-2 loop before the top-K reads them), so nothing left
+  // by an earlier call needs clearing.
   return mcs_select(d, q, k, perm, lse, idx, ws, (size_t)MCS_SCRATCH_BYTES, stream);
 }
 

@@ -654,12 +654,11 @@ hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s) {
-  hipError_t e;
-  if (dtype == DT_BF16)
-    e = head_dim == 128 ? launch_mass_lds<128>(a, s) : launch_mass_lds<64>(a, s);
-  else
-    e = head_dim == 128 ? launch_mass_t<float, 128>(a, s) : launch_mass_t<float, 64>(a, s);
-  if (e != hipSuccess) return e;
+  if (dtype == DT_BF16) return head_dim == 128 ? launch_mass_lds<128>(a, s) : launch_mass_lds<64>(a, s);
+  return head_dim == 128 ? launch_mass_t<float, 128>(a, s) : launch_mass_t<float, 64>(a, s);
+}
+
+hipError_t launch_topk(const MassArgs& a, hipStream_t s) {
   const int rows = a.hcount * a.G;
   hipLaunchKernelGGL(topk_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();

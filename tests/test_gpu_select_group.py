@@ -175,3 +175,30 @@ def test_select_full_density_keeps_everything():
     perm = np.arange(n, dtype=np.int32)[None]
     idx = host(mcs.mcs_select(to_dev(q, "bf16"), to_dev(k, "bf16"), torch.from_numpy(perm).to(dev()), n))
     assert (idx[:, :, :n] == np.arange(n)).all()
+
+
+@pytest.mark.parametrize("lse_given", [False, True])
+def test_select_head_passes_give_the_same_lists(lse_given):
+    """Heads are selected in passes of as many as the workspace holds (mass rows
+    and their histograms, then the top-K of the pass).  Every pass size gives the
+    same index lists, also with no host synchronisation between calls, and so
+    does the entry point that allocates nothing.  The lists match the oracle."""
+    wl = W.Workload("t", (5, 9, 23), 7, 128, "bf16", 64, (0.2,), 13, 0.0, 0)
+    q, k, _ = W.make_qkv(wl)
+    qd, kd = to_dev(q, "bf16"), to_dev(k, "bf16")
+    kk = wl.topk(0.2)
+    perm = mcs.mcs_group(qd)
+    lse = mcs.mcs_dense_attn(qd, kd, to_dev(np.zeros_like(q), "bf16"), want_lse=True)[1] if lse_given else None
+    outs = {hpp: mcs.mcs_select(qd, kd, perm, kk, lse=lse, heads_per_pass=hpp) for hpp in (1, 2, 3, 4, 6, 0)}
+    again = mcs.mcs_select(qd, kd, perm, kk, lse=lse)
+    noalloc = mcs.mcs_select_noalloc(qd, kd, perm, kk, lse=lse)
+    torch.cuda.synchronize()
+    for hpp, idx in outs.items():
+        assert torch.equal(idx, outs[1]), f"heads_per_pass={hpp}"
+    assert torch.equal(again, outs[1]) and torch.equal(noalloc, outs[1])
+    s = 1.0 / np.sqrt(wl.head_dim)
+    p, ih = host(perm), host(outs[1])
+    for h in (0, wl.heads - 1):
+        mass = ref.group_mass(q[h], k[h], ref.row_lse(q[h], k[h], s), p[h], 64, s)
+        for g in range(wl.groups):
+            check_index_row(ih[h, g], mass[g], kk, wl.n)
