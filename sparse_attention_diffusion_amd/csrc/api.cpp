@@ -72,7 +72,7 @@ int check_ptr(const void* p, size_t align, const char* name) {
 size_t stats_bytes(const mcs_dims* d) { return align256((size_t)d->heads * d->n * 8); }
 int mass_ld(const mcs_dims* d) { return (d->n + 3) & ~3; }
 size_t mass_rows_bytes_per_head(const mcs_dims* d) { return align256((size_t)groups_of(d) * mass_ld(d) * 4); }
-constexpr size_t kHistBytesPerGroup = 4096 * 4;  // a mass row's 12-bit histogram
+constexpr size_t kHistBytesPerGroup = (size_t)mcs::kMassHistBins * 4;  // a mass row's histogram
 size_t mass_bytes_per_head(const mcs_dims* d) {
   return mass_rows_bytes_per_head(d) + align256((size_t)groups_of(d) * kHistBytesPerGroup);
 }

@@ -47,6 +47,7 @@ hipError_t launch_pair_plan(const int32_t* idx, int32_t* pidx, int32_t* ncommon,
 // Selection pass 2 with the per-group top-K fused into its epilogue: summed
 // normalised probabilities of every key per query group (written to `mass`),
 // then the K keys of largest mass per group, ascending, -1 padded to kpad.
+constexpr int kMassHistBins = 2048;  // bins of a mass row's histogram (top 11 value bits)
 struct MassArgs {
   const void* q;
   const void* k;
@@ -54,7 +55,7 @@ struct MassArgs {
   const float2* stats;     // [H][N] row statistics from pass 1 (or null: use lse)
   const float* lse;        // [H][N] natural-log logsumexp (used when stats is null)
   float* mass;             // [hcount][G][ldm] scratch rows
-  uint32_t* hist;          // [hcount][G][4096] scratch: each row's histogram of its top 12 value bits
+  uint32_t* hist;          // [hcount][G][kMassHistBins] scratch: each row's histogram of its top value bits
   int ldm;                 // row stride of mass: N rounded up to a multiple of 4
   int32_t* idx;            // [H][G][kpad] output
   int h0, hcount, N, G, K, kpad;

@@ -8,7 +8,7 @@
 // all keys, 32 at a time (v_mfma_f32_32x32x16_bf16 with the group's queries as
 // the A operand, so each lane owns one key column), normalises each logit with
 // its row statistics and sums the 64 probabilities per key: mass[g][j].
-// While the row is produced, a 4096-bin histogram of its top 12 value bits is
+// While the row is produced, a 2048-bin histogram of its top 11 value bits is
 // built in LDS (non-negative floats order like their bit patterns) and stored
 // beside the row when the loop ends.
 // Top-K (a second kernel, four waves per SIMD so that the row reads overlap):
@@ -39,8 +39,12 @@ struct QTile {
   __device__ static uint32_t khalf_off(int hf) { return F32 ? (uint32_t)(D / 2 * 4 * hf) : (uint32_t)(16 * hf); }
 };
 
-// The loop's histogram: 4096 bins of the top 12 value bits (30..19) of a mass.
-constexpr int kHistBins = 4096;
+// The loop's histogram: kMassHistBins bins of the top 11 value bits (30..20) of
+// a mass (bit 31, the sign, is clear).
+constexpr int kHistBins = kMassHistBins;
+constexpr int kHistShift = 20;
+constexpr int kHistPerLane = kHistBins / 64;
+static_assert(kHistBins == 1 << (31 - kHistShift), "bins = bits 30..kHistShift");
 // Per-wave shared memory of the top-K: a 256-bin histogram for refining the
 // threshold, and the values of the candidates (entries of the threshold's bin),
 // in ascending key order.
@@ -116,7 +120,7 @@ __device__ uint32_t pick_digit(const uint32_t* hist, int bins, uint32_t& kr, uin
   return (uint32_t)d;
 }
 
-constexpr int kMassStages = 6;  // K tiles in flight in the bf16 pass-2 loop
+constexpr int kMassStages = 4;  // K tiles in flight in the bf16 pass-2 loop
 constexpr int kUnroll = 4;
 constexpr int kBatch = 256 * kUnroll;
 
@@ -155,10 +159,10 @@ __device__ __forceinline__ void scan_row(const uint32_t* rb, int N, F&& f) {
   if (base < N) f(base, ba);
 }
 
-// Bin (from the top) of a stored 4096-bin histogram that holds the kr-th
-// largest entry (1-based); leaves in kr the rank inside that bin and in cnt its
-// population.  Lane l sums bins [64l, 64l + 64); suffix sums over the lanes find
-// the lane, then over that lane's 64 bins the bin.
+// Bin (from the top) of a stored histogram that holds the kr-th largest entry
+// (1-based); leaves in kr the rank inside that bin and in cnt its population.
+// Lane l sums its kHistPerLane consecutive bins; suffix sums over the lanes find
+// the lane, then over that lane's bins the bin.
 __device__ uint32_t pick_top_bin(const uint32_t* gh, uint32_t& kr, uint32_t& cnt) {
   const int lane = threadIdx.x & 63;
   auto suffix = [&](uint32_t x) {  // inclusive: sum over lanes >= this one
@@ -169,10 +173,10 @@ __device__ uint32_t pick_top_bin(const uint32_t* gh, uint32_t& kr, uint32_t& cnt
     }
     return x;
   };
-  const u32x4* p = reinterpret_cast<const u32x4*>(gh + 64 * lane);
+  const u32x4* p = reinterpret_cast<const u32x4*>(gh + kHistPerLane * lane);
   uint32_t t = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < kHistPerLane / 4; ++i) {
     const u32x4 v = p[i];
     t += v[0] + v[1] + v[2] + v[3];
   }
@@ -181,27 +185,27 @@ __device__ uint32_t pick_top_bin(const uint32_t* gh, uint32_t& kr, uint32_t& cnt
   uint64_t m = __builtin_amdgcn_ballot_w64(inc >= kr && inc - t < kr);
   const int L = m ? __builtin_ctzll(m) : 0;
   uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(inc - t), L);
-  const uint32_t c = gh[64 * L + lane];
+  const uint32_t c = lane < kHistPerLane ? gh[kHistPerLane * L + lane] : 0u;
   inc = suffix(c) + above;
   m = __builtin_amdgcn_ballot_w64(inc >= kr && inc - c < kr);
   const int j = m ? __builtin_ctzll(m) : 0;
   cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
   kr -= (uint32_t)__builtin_amdgcn_readlane((int)(inc - c), j);
-  return (uint32_t)(64 * L + j);
+  return (uint32_t)(kHistPerLane * L + j);
 }
 
 // Exact top-K of one mass row by one wavefront, ascending ids, ties to the lower
-// id.  gh is the row's stored 12-bit histogram.  The row's head is overwritten
-// by the provisional list.
+// id.  gh is the row's stored histogram.  The row's head is overwritten by the
+// provisional list.
 __device__ void wave_topk(float* row, const uint32_t* gh, int N, int K, int kpad, int32_t* out, WaveTopk* w) {
   const int lane = threadIdx.x & 63;
   uint32_t* rb = reinterpret_cast<uint32_t*>(row);
   uint32_t kr = (uint32_t)K, cnt = 0;
-  uint32_t prefix = pick_top_bin(gh, kr, cnt) << 19;
-  uint32_t pmask = 0xfffu << 19;
-  int shift = 19;
+  uint32_t prefix = pick_top_bin(gh, kr, cnt) << kHistShift;
+  uint32_t pmask = (uint32_t)(kHistBins - 1) << kHistShift;
+  int shift = kHistShift;
   // Refine the prefix while too many entries share it, 8 bits per pass (common
-  // when the masses near the threshold are dense: a 12-bit bin then holds
+  // when the masses near the threshold are dense: an 11-bit bin then holds
   // thousands of entries).  The row is read in the same batches as below.
   while (cnt > (uint32_t)kCandCap && shift > 0) {
     const int nshift = shift >= 8 ? shift - 8 : 0;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
     acc = pair_sum(acc);
     if (hf == 0 && t0 + lm < N) {
       out[t0 + lm] = acc;
-      atomicAdd(&hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
+      atomicAdd(&hist[__float_as_uint(acc) >> kHistShift], 1u);  // non-negative: bit 31 clear
     }
   };
   // Software pipeline: the MFMAs of step i+1 are issued before the exponentials
@@ -480,12 +484,13 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
 // consumed" from the reads.  This cuts the address work of the K fetches by
 // 16x (quad-contiguous copies, a quarter each) and the L2 traffic by 4x.
 //
-// With one block per CU, the copies in flight set the pace: two 8 KiB stages
-// held the loop at about 4 TB/s of K, at the copy latency, whatever the math.
-// So the tiles rotate through NS = 6 stages, copied NS steps ahead, after the
-// four waves' histograms.
+// A wave issues in order, so its own MFMAs and VALU do not overlap: two blocks
+// per CU (two waves per SIMD, from blocks with no barrier between them) let one
+// wave's exponentials run beside the other's MFMAs.  That caps a block at 64 KB
+// of LDS: four 8 KiB stages, copied four steps ahead, after the four waves'
+// 8 KiB histograms.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void group_mass_lds_kernel(MassArgs a) {
   using L = LT<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -587,7 +592,7 @@ void group_mass_lds_kernel(MassArgs a) {
     uint32_t soff = keep ? (uint32_t)(t0 + lm) * 4u : 0xfffffff0u;
     asm volatile("" : "+v"(soff));  // opaque: keeps the store out of the branch on `keep`
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rout, soff, 0, 0);
-    if (keep) lds_add_u32(&hist[__float_as_uint(acc) >> 19], 1u);  // non-negative: bit 31 clear
+    if (keep) lds_add_u32(&hist[__float_as_uint(acc) >> kHistShift], 1u);  // non-negative: bit 31 clear
   };
   // Iteration i: barrier (every wave's copy of K(i+1) landed, every wave done
   // with K(i)'s stage), copy K(i+NS) into that stage, QK of step i+1, then the
