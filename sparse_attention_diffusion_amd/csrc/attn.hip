@@ -947,11 +947,16 @@ __device__ __forceinline__ void lqueries(int (&tokq)[2], bool (&qvalid)[2], u32x
   }
 }
 
+// Bytes of one stage: K and V tiles (also the epilogue's O buffer) with the PV
+// product, the K tile alone without it.
+template <int D, bool PV>
+constexpr int stage_bytes() { return PV ? LT<D>::STAGE : LT<D>::TILE; }
+
 // Stages start zeroed: a padding entry's copy may leave its slot untouched,
 // and a masked probability times a stale non-finite value would poison O.
-template <int D>
+template <int D, bool PV = true>
 __device__ __forceinline__ void lzero(LDSP char* s0, LDSP char* s1, int lane) {
-  for (int o = lane * 16; o < LT<D>::STAGE; o += 64 * 16) {
+  for (int o = lane * 16; o < stage_bytes<D, PV>(); o += 64 * 16) {
     *(LDSP u32x4*)(s0 + o) = u32x4{0, 0, 0, 0};
     *(LDSP u32x4*)(s1 + o) = u32x4{0, 0, 0, 0};
   }
@@ -1003,12 +1008,16 @@ __device__ __forceinline__ void lend(const LState<D, PV>& st, const LCtx<D>& x, 
 
 // STATS (dense with PV only): also keep the exact row sums for the statistics;
 // the other variants have one sum (see row_sums).
+// Without the PV product (selection pass 1, sparse logsumexp) a stage holds only
+// the K tile, so two blocks fit a CU: a wave issues in order and its own MFMAs
+// and VALU do not overlap, but a second wave per SIMD runs its exponentials
+// beside the first one's MFMAs.
 template <int D, bool GATHER, int EPI, bool PV, bool STATS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PV ? 1 : 2, PV ? 1 : 2)))
 void attn_lds_kernel(AttnArgs a) {
   using L = LT<D>;
-  __shared__ __attribute__((aligned(16))) char stage0[4][L::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage1[4][L::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage0[4][stage_bytes<D, PV>()];
+  __shared__ __attribute__((aligned(16))) char stage1[4][stage_bytes<D, PV>()];
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int items = a.H * a.G;
   const int blk = xcd_remap(blockIdx.x, (items + 3) >> 2, a.xcd_chunk);
@@ -1026,7 +1035,7 @@ void attn_lds_kernel(AttnArgs a) {
   bool qvalid[2];
   u32x4 q[2][L::KCH];
   lqueries<D>(tokq, qvalid, q, a, rq, h, g, lane);
-  lzero<D>(s0, s1, lane);
+  lzero<D, PV>(s0, s1, lane);
   LState<D, PV> st;
   lstate_init<D, PV>(st);
   if (x.nkeys > 0) lpass<D, GATHER, PV, STATS>(st, x, q, s0, s1);
