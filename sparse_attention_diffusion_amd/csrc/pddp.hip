@@ -57,8 +57,12 @@ __host__ __device__ inline Node walk_node(int N, int C, int level, int k) {
   return nd;
 }
 
+// One level of the tree as launched: `nodes` blocks (times `parts`) per head.
+// With `list`, block j of a head takes node list[j] (the level's internal nodes,
+// listed on the device when the level also holds leaves); otherwise node j.
 struct Level {
   int level, nodes, parts;
+  const int32_t* list;
 };
 
 // Workspace carve-up (all offsets 256-byte aligned).
@@ -67,6 +71,7 @@ struct Ws {
   uint32_t* keys;      // [H][N]
   float* partials;     // [H][kMaxParts][D + D*D]
   float* node_param;   // [H][max_nodes][2*D]   (mu, v)
+  int32_t* node_list;  // [max_nodes]: the internal nodes of the current level
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -92,7 +97,7 @@ inline int parts_for(int N, int level) {
   return p < 1 ? 1 : p;
 }
 
-inline Ws carve(void* base, int H, int N, int D) {
+inline Ws carve(void* base, int H, int N, int D, int C) {
   char* p = (char*)base;
   Ws w;
   w.tmp_perm = (int32_t*)p;
@@ -102,6 +107,8 @@ inline Ws carve(void* base, int H, int N, int D) {
   w.partials = (float*)p;
   p += align256((size_t)H * kMaxParts * (D + (size_t)D * D) * 4);
   w.node_param = (float*)p;
+  p += align256((size_t)H * max_nodes(N, C) * 2 * D * 4);
+  w.node_list = (int32_t*)p;
   return w;
 }
 
@@ -201,22 +208,37 @@ __device__ __forceinline__ void load_dims(const T* p, float* out) {
 }
 
 // Projection keys of slots [r0, r1): key = float_key((x - mu) . v), 16 lanes per
-// row, D/16 consecutive dims per lane (lane `sub` holds mu and v of its dims).
+// row, D/16 consecutive dims per lane.  Each thread has the perm entries and then
+// the rows of kRowsInFlight slots in flight before it reduces any of them (one
+// slot at a time left the pass bound by the perm -> row load latency).
+constexpr int kRowsInFlight = 4;
 template <typename T, int D>
 __device__ __forceinline__ void project_rows(const T* qh, const int32_t* permh, uint32_t* keys, int r0, int r1,
                                              const float (&mu)[D / 16], const float (&v)[D / 16]) {
   constexpr int DPL = D / 16;
+  constexpr int RSTEP = kThreads / 16;
+  constexpr int U = kRowsInFlight;
   const int tid = threadIdx.x, sub = tid & 15, rgrp = tid >> 4;
-  for (int row = r0 + rgrp; row < r1; row += kThreads / 16) {
-    const int tok = permh[row];
-    float x[DPL];
-    load_dims<T, DPL>(qh + (size_t)tok * D + sub * DPL, x);
-    float p = 0.0f;
+  for (int row0 = r0 + rgrp; row0 < r1; row0 += U * RSTEP) {
+    int tok[U];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(x[j] - mu[j], v[j], p);
+    for (int u = 0; u < U; ++u) {
+      const int row = row0 + u * RSTEP;
+      tok[u] = row < r1 ? permh[row] : 0;  // past the range: any row of the head, not stored
+    }
+    float x[U][DPL];
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
-    if (sub == 0) keys[row] = float_key(p);
+    for (int u = 0; u < U; ++u) load_dims<T, DPL>(qh + (size_t)tok[u] * D + sub * DPL, x[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float p = 0.0f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) p = __builtin_fmaf(x[u][j] - mu[j], v[j], p);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
+      const int row = row0 + u * RSTEP;
+      if (sub == 0 && row < r1) keys[row] = float_key(p);
+    }
   }
 }
 
@@ -383,7 +405,8 @@ __global__ __launch_bounds__(kThreads) void pddp_stats_kernel(PddpArgs a, Ws w, 
   const int per_head = lv.nodes * P;
   const int h = blockIdx.x / per_head;
   const int rem = blockIdx.x - h * per_head;
-  const int k = rem / P, part = rem - k * P;
+  const int kk = rem / P, part = rem - kk * P;  // kk: launch index, k: node id
+  const int k = lv.list ? lv.list[kk] : kk;
   const Node nd = walk_node(a.N, a.C, lv.level, k);
   if (!nd.internal) return;
   const int chunk = (nd.n + P - 1) / P;
@@ -403,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void pddp_stats_kernel(PddpArgs a, Ws w, 
   float colsum;
   stats_rows<T, D>(qh, permh, vec, r0, max(r1, r0), tile, sa, colsum);
   if (P > 1) {
-    float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)k * P + part) * (D + (size_t)D * D);
+    float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)kk * P + part) * (D + (size_t)D * D);
     if (tid < D) dst[tid] = colsum;
     store_acc<D, SA::TPW>(sa.acc, acc_ta<D>(wid), acc_tb0<D>(wid), dst + D);
     return;
@@ -423,7 +446,8 @@ __global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, 
   extern __shared__ float smem[];  // PowLds<D>
   constexpr int TPW = (D / 32) * (D / 32) / 4;
   const int h = blockIdx.x / lv.nodes;
-  const int k = blockIdx.x - h * lv.nodes;
+  const int kk = blockIdx.x - h * lv.nodes;  // launch index; k: node id
+  const int k = lv.list ? lv.list[kk] : kk;
   const Node nd = walk_node(a.N, a.C, lv.level, k);
   if (!nd.internal) return;
   const int P = lv.parts;
@@ -431,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void pddp_power_kernel(PddpArgs a, Ws w, 
   const int32_t* permh = a.perm + (size_t)h * a.N;
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), hf = lane >> 5, lm = lane & 31;
   const size_t stride = D + (size_t)D * D;
-  const float* src = w.partials + ((size_t)h * kMaxParts + (size_t)k * P) * stride;
+  const float* src = w.partials + ((size_t)h * kMaxParts + (size_t)kk * P) * stride;
   float* vec = smem + PowLds<D>::VEC;
   if (tid < D) {
     float s = 0.0f;
@@ -527,7 +551,8 @@ void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
   const int per_head = lv.nodes * P;
   const int h = blockIdx.x / per_head;
   const int rem = blockIdx.x - h * per_head;
-  const int k = rem / P, part = rem - k * P;
+  const int kk = rem / P, part = rem - kk * P;  // kk: launch index, k: node id
+  const int k = lv.list ? lv.list[kk] : kk;
   const Node nd = walk_node(a.N, a.C, lv.level, k);
   if (!nd.internal) return;
   const int chunk = (nd.n + P - 1) / P;
@@ -649,7 +674,7 @@ void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
     for (int rr = 0; rr < B::RSTEP; ++rr) colsum += csp[rr * D + tid];
 
   if (P > 1) {
-    float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)k * P + part) * (D + (size_t)D * D);
+    float* dst = w.partials + ((size_t)h * kMaxParts + (size_t)kk * P + part) * (D + (size_t)D * D);
     if (tid < D) dst[tid] = colsum;
     store_acc<D, B::TPW>(acc, ta, tb0, dst + D);
     return;
@@ -673,7 +698,8 @@ __global__ __launch_bounds__(kThreads) void pddp_project_kernel(PddpArgs a, Ws w
   const int per_head = lv.nodes * P;
   const int h = blockIdx.x / per_head;
   const int rem = blockIdx.x - h * per_head;
-  const int k = rem / P, part = rem - k * P;
+  const int kk = rem / P, part = rem - kk * P;  // kk: launch index, k: node id
+  const int k = lv.list ? lv.list[kk] : kk;
   const Node nd = walk_node(a.N, a.C, lv.level, k);
   if (!nd.internal) return;
   const int chunk = (nd.n + P - 1) / P;
@@ -783,7 +809,8 @@ __global__ __launch_bounds__(NT) void pddp_split_kernel(PddpArgs a, Ws w, Level 
   __shared__ uint32_t wsum[NT / 64];
   __shared__ uint32_t bcast[2];
   const int h = blockIdx.x / lv.nodes;
-  const int k = blockIdx.x - h * lv.nodes;
+  const int kk = blockIdx.x - h * lv.nodes;  // launch index; k: node id
+  const int k = lv.list ? lv.list[kk] : kk;
   const Node nd = walk_node(a.N, a.C, lv.level, k);
   if (!nd.internal) return;
   const int g = (nd.n + a.C - 1) / a.C;
@@ -858,6 +885,22 @@ __global__ __launch_bounds__(NT) void pddp_split_kernel(PddpArgs a, Ws w, Level 
   }
 }
 
+// The internal nodes of `level` (those still holding two or more groups) in
+// ascending order, for a level that also holds leaves: one block.
+__global__ __launch_bounds__(1024) void pddp_list_kernel(int N, int C, int level, int32_t* list) {
+  __shared__ uint32_t wsum[1024 / 64];
+  const int nodes = 1 << level;
+  uint32_t done = 0;
+  for (int b = 0; b < nodes; b += 1024) {
+    const int k = b + (int)threadIdx.x;
+    const bool f = k < nodes && walk_node(N, C, level, k).internal;
+    uint32_t incl;
+    const uint32_t tot = block_scan<1024>(f ? 1u : 0u, wsum, incl);
+    if (f) list[done + incl - 1] = k;
+    done += tot;
+  }
+}
+
 __global__ void iota_kernel(int32_t* perm, int H, int N) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < (size_t)H * N) perm[i] = (int32_t)(i % (size_t)N);
@@ -865,7 +908,7 @@ __global__ void iota_kernel(int32_t* perm, int H, int N) {
 
 template <typename T, int D>
 hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
-  Ws w = carve(a.ws, a.H, a.N, D);
+  Ws w = carve(a.ws, a.H, a.N, D, a.C);
   const size_t total = (size_t)a.H * a.N;
   hipLaunchKernelGGL(iota_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.perm, a.H, a.N);
   hipError_t e = hipGetLastError();
@@ -874,7 +917,17 @@ hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
   const size_t lds_f32 = (size_t)stats_f32_lds_floats<T, D>() * sizeof(float);
   const size_t lds_pow = (size_t)PowLds<D>::FLOATS * sizeof(float);
   for (int l = 0; l < L; ++l) {
-    Level lv{l, 1 << l, parts_for(a.N, l)};
+    // internal nodes of the level, counted on the host (the tree depends only on N, C)
+    int internal = 0;
+    for (int k = 0; k < (1 << l); ++k) internal += walk_node(a.N, a.C, l, k).internal ? 1 : 0;
+    Level lv{l, 1 << l, parts_for(a.N, l), nullptr};
+    if (internal < lv.nodes) {  // the level also holds leaves: launch its internal nodes only
+      hipLaunchKernelGGL(pddp_list_kernel, dim3(1), dim3(1024), 0, s, a.N, a.C, l, w.node_list);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      lv.nodes = internal;
+      lv.list = w.node_list;
+    }
+    if (lv.nodes == 0) continue;
     const unsigned nb = (unsigned)(a.H * lv.nodes * lv.parts);
     if constexpr (std::is_same<T, __bf16>::value)
       hipLaunchKernelGGL((pddp_stats_bf16_kernel<D>), dim3(nb), dim3(kThreads), BStats<D>::BYTES, s, a, w, lv);
@@ -904,7 +957,7 @@ hipError_t run_levels(const PddpArgs& a, hipStream_t s) {
 
 size_t pddp_workspace_bytes(int H, int N, int D, int C) {
   return align256((size_t)H * N * 4) * 2 + align256((size_t)H * kMaxParts * (D + (size_t)D * D) * 4) +
-         align256((size_t)H * max_nodes(N, C) * 2 * D * 4);
+         align256((size_t)H * max_nodes(N, C) * 2 * D * 4) + align256((size_t)max_nodes(N, C) * 4);
 }
 
 hipError_t launch_pddp(const PddpArgs& a, int dtype, hipStream_t s) {
