@@ -169,6 +169,25 @@ def test_select_group_of_equal_logits_ties_to_lowest_ids():
     assert (idx[:, :, 37:] == -1).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kk", [100, 3000])
+def test_select_more_equal_masses_than_the_candidate_list_holds(dtype, kk):
+    # Q = 0: every key of a group gets the same mass |g| / N, computed the same way,
+    # so 5,000 entries share the threshold value: more than the top-K's 2,048-entry
+    # candidate list.  The threshold resolves to that value and the first K ids are
+    # kept, also when K itself is past the list's size.
+    n, d = 5000, 128
+    q = np.zeros((2, n, d), np.float32)
+    k = W.store(np.random.default_rng(3).standard_normal((2, n, d)), dtype)
+    perm = np.stack([np.random.default_rng(4 + h).permutation(n) for h in range(2)]).astype(np.int32)
+    qd, kd = to_dev(q, dtype), to_dev(k, dtype)
+    pd = torch.from_numpy(perm).to(dev())
+    for idx in (mcs.mcs_select(qd, kd, pd, kk), mcs.mcs_select_noalloc(qd, kd, pd, kk)):
+        idx = host(idx)
+        assert (idx[:, :, :kk] == np.arange(kk)).all()
+        assert (idx[:, :, kk:] == -1).all()
+
+
 def test_select_full_density_keeps_everything():
     q, k, _ = _grid_qk((2, 5, 10), 1, 128, "bf16", seed=4)
     n = q.shape[1]
