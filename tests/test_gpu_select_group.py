@@ -188,6 +188,30 @@ def test_select_more_equal_masses_than_the_candidate_list_holds(dtype, kk):
         assert (idx[:, :, kk:] == -1).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_select_refines_a_crowded_threshold_bin(dtype):
+    # Small logits: the masses of a group lie within about 2% of each other, so
+    # nearly all 6,000 keys share one 11-bit histogram bin (1/8 relative width) and
+    # the top-K narrows the threshold with passes over the row before it can list
+    # the candidates.  Index sets against the oracle's masses.
+    n, d, kk = 6000, 64, 1500
+    r = np.random.default_rng(11)
+    u = r.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = W.store(np.tile(0.02 * u, (1, n, 1)) + 1e-4 * r.standard_normal((1, n, d)), dtype)
+    k = W.store(r.standard_normal((1, n, d)), dtype)
+    perm = r.permutation(n).astype(np.int32)[None]
+    s = 1.0 / np.sqrt(d)
+    idx = host(mcs.mcs_select(to_dev(q, dtype), to_dev(k, dtype), torch.from_numpy(perm).to(dev()), kk))
+    lse = ref.row_lse(q[0], k[0], s)
+    mass = ref.group_mass(q[0], k[0], lse, perm[0], 64, s)
+    bins = np.asarray(mass[0], np.float32).view(np.uint32) >> 20  # the top 11 value bits
+    crowd = int(np.unique(bins, return_counts=True)[1].max())
+    ties = sum(check_index_row(idx[0, g], mass[g], kk, n) for g in range(mass.shape[0]))
+    print(f"{dtype}: {crowd} of group 0's {n} masses share one 11-bit bin; {ties} keys within the tie window")
+    assert crowd > 2048  # the construction does crowd the bin past the candidate list
+
+
 def test_select_full_density_keeps_everything():
     q, k, _ = _grid_qk((2, 5, 10), 1, 128, "bf16", seed=4)
     n = q.shape[1]
