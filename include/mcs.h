@@ -89,8 +89,9 @@ const char* mcs_last_error(void);
 
 /* Workspace needed by op (MCS_OP_GROUP / SELECT / ANCHOR / BLOCK_SELECT) when up to
  * heads_per_pass heads of the selection mass are processed at once
- * (0 = all heads).  The selection stores one fp32 mass row of N entries per
- * group for each head of a pass, so heads_per_pass bounds the memory.  Any
+ * (0 = all heads).  The selection stores one fp32 mass row of N entries and an
+ * 8 KB histogram per group for each head of a pass, so heads_per_pass bounds
+ * the memory.  Any
  * workspace at least as large as the heads_per_pass = 1 figure is accepted by
  * the calls below; larger ones process more heads per pass. */
 int mcs_workspace_bytes(const mcs_dims* d, int32_t op, int32_t heads_per_pass, size_t* bytes);
@@ -120,7 +121,8 @@ int mcs_select(const mcs_dims* d, const void* q, const void* k, const int32_t* p
  * that each GPU the library runs on holds until the process ends.  Processes
  * ceil(H / hpp) passes of hpp heads, hpp as large as the scratch allows.
  * Workloads needing more than MCS_SCRATCH_BYTES for one head (8*H*N bytes of
- * statistics plus about N*N/16 of mass rows, padded) are rejected with
+ * statistics plus about N*N/16 of mass rows and N/8 KB of histograms, padded)
+ * are rejected with
  * MCS_EUNSUPPORTED before any HIP call.  The scratch belongs to the current
  * device (hipSetDevice), which must be the device of `stream` and of every
  * buffer.  Every call on one GPU shares that GPU's scratch: calls that overlap

@@ -62,7 +62,7 @@ struct MassArgs {
   float c;                 // scale * log2(e)
   int xcd_chunk;
 };
-// Pass 2: the mass rows and their 12-bit histograms of heads h0 .. h0+hcount-1.
+// Pass 2: the mass rows and their histograms of heads h0 .. h0+hcount-1.
 hipError_t launch_group_mass(const MassArgs& a, int dtype, int head_dim, hipStream_t s);
 // Exact top-K of those rows into idx (reads the rows and histograms; overwrites the rows).
 hipError_t launch_topk(const MassArgs& a, hipStream_t s);
