@@ -154,7 +154,7 @@ def sdpa_context(q, k, v, reps=3):
             evs = [_timed(f, s)[1] for _ in range(reps)]
             torch.cuda.synchronize()
             return sum(a.elapsed_time(b) for a, b in evs) / reps
-    except Exception as e:  # backend unavailable on this build: report nothing
+    except Exception as e:  # backend unavailable in this torch: report nothing
         print(f"[bench] torch SDPA context unavailable: {type(e).__name__}: {e}", file=sys.stderr)
         return None
 
@@ -174,8 +174,8 @@ def main():
                     help="copy 1 GiB once before the workload (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the MC-Sparse hot path is built and timed on a single MI355X "
-              "(heads shard across GPUs without any exchange; no multi-GPU run is part of this build).",
+        print("bench.py measures one GPU: the MC-Sparse hot path runs and is timed on a single MI355X "
+              "(heads shard across GPUs without any exchange; there is no multi-GPU code path).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -81,7 +81,7 @@ def _sharp_case(seed):
 @pytest.mark.parametrize("seed", range(12))
 def test_sharp_attention_random_shape_within_derived_bound(seed):
     # Logit std about 5 (q, k ~ N(0, 5) per component, scale 1/sqrt(D)): rows close to
-    # one-hot, |O| up to the 4-8 binade.  bf16 outputs are held to the north-star
+    # one-hot, |O| up to the 4-8 binade.  bf16 outputs are held to the 2e-2 / 2e-3
     # tolerances and, element by element, to the bound derived from the arithmetic
     # (tests/gpu_util.py: bf16 rounding of the probabilities, normalised by the sum of
     # the same rounded values, plus half an ulp of the output).  Index sets use a tie
