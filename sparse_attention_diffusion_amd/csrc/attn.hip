@@ -1184,6 +1184,150 @@ void attn_pairs_kernel(AttnArgs a, const int32_t* ncommon) {
   lend<D, true, EPI, true, false>(st, x, a, rq, h, tokq, qvalid, lane, own0);
 }
 
+// ---------------------------------------------------------------------------
+// Dense attention at two blocks per CU.  A wave issues in order, so its own MFMAs
+// and its softmax VALU do not overlap; at one wave per SIMD a step costs both.
+// Here a block's four waves take four 64-query groups of one head and share a
+// ring of kDenseStages K/V stages (every group of a head reads every key in the
+// same order): each wave issues a quarter of each step's copies, and one block
+// barrier per step marks "this step's copies landed everywhere, the stage read two
+// steps ago is free".  With the K and V operands read from LDS chunk by chunk next
+// to the MFMAs that use them (not all eight chunks at once), a wave fits in 256
+// registers, so two blocks share a CU and the two waves of a SIMD, from different
+// blocks, run one's exponentials beside the other's MFMAs.  Per query the
+// arithmetic is that of the one-wave-per-SIMD kernel, in the same order.
+constexpr int kDenseStages = 4;
+
+// One step of a 64-query wave on stage `cur` (no copies, no waits).
+template <int D, bool STATS, bool FIRST, bool LAST>
+__device__ __forceinline__ void rstep(LState<D, true>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
+                                      const LDSP char* cur, int it) {
+  using L = LT<D>;
+  typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < L::KCH; ++ks) {
+    const u32x4 ka = *(const LDSP u32x4*)(cur + x.kaddr[ks & 1] + 64 * (ks >> 1));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) s[nt] = mfma_bf16(as_bf16x8(ka), as_bf16x8(q[nt][ks]), s[nt]);
+  }
+  if constexpr (LAST) lmask(s, it * 32, x.nkeys, x.hf);
+  if constexpr (FIRST) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = s[nt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+      st.m[nt] = pair_max(mx) * x.c + kMargin;
+    }
+  }
+  uint32_t pk[2][8];
+  lprobs<D, true, STATS>(st, s, pk, x.c);
+  const LDSP char* vt = cur + L::TILE;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    bf16x8 pa[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pk[nt][4 * kc + i];
+      pa[nt] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int n = 0; n < L::VT; ++n) {
+      const bf4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + x.vaddr[kc][0] + 64 * n));
+      const bf4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + x.vaddr[kc][1] + 64 * n));
+      const bf16x8 vb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) st.o[nt][n] = mfma_bf16(pa[nt], vb, st.o[nt][n]);
+    }
+  }
+}
+
+// This wave's quarter of the copies of step j (K and V tiles) into its ring stage.
+template <int D, int NS>
+__device__ __forceinline__ void ring_copy(LDSP char* ring0, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int j, int ebase, uint32_t goff, int wid) {
+  constexpr int NC = LT<D>::NI / 4;
+  LDSP char* stg = ring0 + (j % NS) * LT<D>::STAGE;
+  tile_copy_dense<D, NC>(stg, rk, j, ebase, goff, wid * NC);
+  tile_copy_dense<D, NC>(stg + LT<D>::TILE, rv, j, ebase, goff, wid * NC);
+}
+
+template <int D, bool STATS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_dense_ring_kernel(AttnArgs a) {
+  using L = LT<D>;
+  constexpr int NS = kDenseStages;
+  constexpr int NC = L::NI / 4;
+  static_assert(NS >= 4, "the epilogue gives each wave one stage");
+  __shared__ __attribute__((aligned(16))) char ring[NS][L::STAGE];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int bph = (a.G + 3) >> 2;  // blocks per head
+  const int blk = xcd_remap(blockIdx.x, a.H * bph, a.xcd_chunk);
+  if (blk < 0) return;  // the whole block
+  const int h = blk / bph;
+  const int g = (blk - h * bph) * 4 + wid;
+  const bool active = g < a.G;
+  const int gc = active ? g : a.G - 1;  // a wave past the last group computes that group and stores nothing
+  const auto rq = make_rsrc((const char*)a.q + (size_t)h * a.N * L::ROWB, (uint32_t)((size_t)a.N * L::ROWB));
+  LCtx<D> x;
+  lctx_init<D, false>(x, a, h, gc, lane);
+  int tokq[2];
+  bool qvalid[2];
+  u32x4 q[2][L::KCH];
+  lqueries<D>(tokq, qvalid, q, a, rq, h, gc, lane);
+  if (!active) qvalid[0] = qvalid[1] = false;
+  // zero the ring before any copy lands (see lzero)
+  for (int o = (wid * 64 + lane) * 16; o < NS * L::STAGE; o += 256 * 16)
+    *(LDSP u32x4*)((LDSP char*)&ring[0][0] + o) = u32x4{0, 0, 0, 0};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  block_barrier();
+  LState<D, true> st;
+  lstate_init<D, true>(st);
+  const int nsteps = (x.nkeys + 31) >> 5;
+  LDSP char* ring0 = (LDSP char*)&ring[0][0];
+  for (int j = 0; j < NS - 1; ++j) ring_copy<D, NS>(ring0, x.rk, x.rv, j, x.ebase, x.goff, wid);
+  // Iteration i: this wave's copies of step i landed (those of the NS - 2 later
+  // steps may still be in flight), then the barrier: everyone's have, and
+  // everyone is done with step i-1, whose stage takes step i+NS-1.  Copies run
+  // past the last step (rows past N read as zeros), so the count in flight is fixed.
+#define MCS_RING_BEGIN(i)                                                    \
+  __builtin_amdgcn_sched_barrier(0);                                         \
+  wait_vm<(NS - 2) * 2 * NC>();                                              \
+  block_barrier();                                                           \
+  ring_copy<D, NS>(ring0, x.rk, x.rv, (i) + NS - 1, x.ebase, x.goff, wid);   \
+  __builtin_amdgcn_sched_barrier(0);
+  if (nsteps == 1) {
+    MCS_RING_BEGIN(0)
+    rstep<D, STATS, true, true>(st, x, q, ring0, 0);
+  } else {
+    MCS_RING_BEGIN(0)
+    rstep<D, STATS, true, false>(st, x, q, ring0, 0);
+    int it = 1;
+#pragma unroll 1
+    for (; it + 1 < nsteps; ++it) {
+      MCS_RING_BEGIN(it)
+      rstep<D, STATS, false, false>(st, x, q, ring0 + (it % NS) * L::STAGE, it);
+    }
+    MCS_RING_BEGIN(it)
+    rstep<D, STATS, false, true>(st, x, q, ring0 + (it % NS) * L::STAGE, it);
+  }
+#undef MCS_RING_BEGIN
+  wait_vm<0>();
+  block_barrier();  // every wave is done with the ring before it holds the epilogue's rows
+  if (!active) return;
+  lend<D, false, EPI_PLAIN, true, STATS>(st, x, a, rq, h, tokq, qvalid, lane, ring0 + wid * L::STAGE);
+}
+
+template <int D, bool STATS>
+hipError_t launch_dense_ring(const AttnArgs& a, hipStream_t s) {
+  const int blocks = xcd_grid(a.H * ((a.G + 3) / 4));
+  hipLaunchKernelGGL((attn_dense_ring_kernel<D, STATS>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, bool GATHER, int EPI, bool PV, bool STATS = false>
 hipError_t launch_lds(const AttnArgs& a, hipStream_t s) {
   const int items = a.H * a.G;
@@ -1228,8 +1372,7 @@ hipError_t launch_d(const AttnArgs& a, bool gather, int epi, bool pv, hipStream_
       }
     }
     // dense: the exact row sums are kept only when statistics are written
-    return (a.stats || a.lse) ? launch_lds<D, false, EPI_PLAIN, true, true>(a, s)
-                              : launch_lds<D, false, EPI_PLAIN, true, false>(a, s);
+    return (a.stats || a.lse) ? launch_dense_ring<D, true>(a, s) : launch_dense_ring<D, false>(a, s);
   } else {
     if (!pv) return gather ? launch_t<T, D, true, EPI_PLAIN, false>(a, s) : launch_t<T, D, false, EPI_PLAIN, false>(a, s);
     if (gather) {
