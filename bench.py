@@ -53,9 +53,10 @@ def sources_sha256() -> str:
 
 
 def committed_traffic(workload: str, density: float):
-    """HBM bytes per launch of the gather-sparse kernel from the committed
-    FETCH_SIZE / WRITE_SIZE summary (calibrated against a copy of known size), or
-    None when there is none or the kernel sources changed since it was taken."""
+    """Memory-fabric bytes per launch of the gather-sparse kernel (L2 misses,
+    MALL hits included, plus writes) from the committed FETCH_SIZE / WRITE_SIZE
+    summary (calibrated against a copy of known size), or None when there is none
+    or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"counters_gather_sparse_{workload}_density{density:g}.md")
     try:
         with open(path) as f:

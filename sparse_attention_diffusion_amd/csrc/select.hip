@@ -8,9 +8,9 @@
 // all keys, 32 at a time (v_mfma_f32_32x32x16_bf16 with the group's queries as
 // the A operand, so each lane owns one key column), normalises each logit with
 // its row statistics and sums the 64 probabilities per key: mass[g][j].
-// While the row is produced, a 2048-bin histogram of its top 11 value bits is
-// built in LDS (non-negative floats order like their bit patterns) and stored
-// beside the row when the loop ends.
+// While the row is produced, a 2048-bin histogram of its values (exponent and
+// top mantissa bits over a window of binades, see hist_bin) is built in LDS and
+// stored beside the row when the loop ends.
 // Top-K (a second kernel, four waves per SIMD so that the row reads overlap):
 // one wavefront per row finds the bin of the K-th largest mass from the stored
 // histogram, then reads the row once.  Every entry above that bin, and every
@@ -39,12 +39,23 @@ struct QTile {
   __device__ static uint32_t khalf_off(int hf) { return F32 ? (uint32_t)(D / 2 * 4 * hf) : (uint32_t)(16 * hf); }
 };
 
-// The loop's histogram: kMassHistBins bins of the top 11 value bits (30..20) of
-// a mass (bit 31, the sign, is clear).
+// The loop's histogram of a row's masses (non-negative floats, whose bit
+// patterns order like their values): bin = exponent and top six mantissa bits
+// (bits 30..17, 1/64 of a binade) over the 32 binades [2^-27, 2^5), values
+// outside that window counted in the end bins.  A row's masses around its K-th
+// largest span a binade or two, so the threshold's bin holds a few hundred
+// entries, which the top-K resolves among themselves after a single read of the
+// row; coarser bins (the top 11 bits) held thousands and cost a second read
+// nearly every time.  A threshold in an end bin is refined from the top bits.
 constexpr int kHistBins = kMassHistBins;
-constexpr int kHistShift = 20;
+constexpr int kHistKeyShift = 17;              // a 15-bit key: bits 31..17 (bit 31 clear)
+constexpr int kHistKeyBase = (127 - 27) << 6;  // key of 2^-27: bin 0
 constexpr int kHistPerLane = kHistBins / 64;
-static_assert(kHistBins == 1 << (31 - kHistShift), "bins = bits 30..kHistShift");
+static_assert(kHistBins == 32 * 64, "32 binades of 64 bins");
+__device__ __forceinline__ uint32_t hist_bin(float mass) {
+  const int key = (int)(__float_as_uint(mass) >> kHistKeyShift) - kHistKeyBase;
+  return (uint32_t)min(max(key, 0), kHistBins - 1);
+}
 // Per-wave shared memory of the top-K: a 256-bin histogram for refining the
 // threshold, and the values of the candidates (entries of the threshold's bin),
 // in ascending key order.
@@ -201,12 +212,26 @@ __device__ void wave_topk(float* row, const uint32_t* gh, int N, int K, int kpad
   const int lane = threadIdx.x & 63;
   uint32_t* rb = reinterpret_cast<uint32_t*>(row);
   uint32_t kr = (uint32_t)K, cnt = 0;
-  uint32_t prefix = pick_top_bin(gh, kr, cnt) << kHistShift;
-  uint32_t pmask = (uint32_t)(kHistBins - 1) << kHistShift;
-  int shift = kHistShift;
-  // Refine the prefix while too many entries share it, 8 bits per pass (common
-  // when the masses near the threshold are dense: an 11-bit bin then holds
-  // thousands of entries).  The row is read in the same batches as below.
+  const uint32_t bin = pick_top_bin(gh, kr, cnt);
+  // The threshold's entries share the top bits of `prefix` under `pmask`; the
+  // bits below `shift` are still open.
+  uint32_t prefix, pmask;
+  int shift;
+  if (bin == 0 || bin == (uint32_t)kHistBins - 1) {
+    // an end bin also counts the values outside the window: start from the top
+    kr = (uint32_t)K;
+    cnt = (uint32_t)N;
+    prefix = 0;
+    pmask = 0;
+    shift = 32;
+  } else {
+    prefix = (bin + (uint32_t)kHistKeyBase) << kHistKeyShift;
+    pmask = 0x7fffu << kHistKeyShift;
+    shift = kHistKeyShift;
+  }
+  // Refine the prefix while too many entries share it, 8 bits per pass (a
+  // threshold in an end bin, or a crowd of nearly equal masses).  The row is read
+  // in the same batches as below.
   while (cnt > (uint32_t)kCandCap && shift > 0) {
     const int nshift = shift >= 8 ? shift - 8 : 0;
     const int bins = 1 << (shift - nshift);
@@ -446,7 +471,7 @@ __global__ __launch_bounds__(256) void group_mass_kernel(MassArgs a) {
     acc = pair_sum(acc);
     if (hf == 0 && t0 + lm < N) {
       out[t0 + lm] = acc;
-      atomicAdd(&hist[__float_as_uint(acc) >> kHistShift], 1u);  // non-negative: bit 31 clear
+      atomicAdd(&hist[hist_bin(acc)], 1u);
     }
   };
   // Software pipeline: the MFMAs of step i+1 are issued before the exponentials
@@ -592,7 +617,7 @@ void group_mass_lds_kernel(MassArgs a) {
     uint32_t soff = keep ? (uint32_t)(t0 + lm) * 4u : 0xfffffff0u;
     asm volatile("" : "+v"(soff));  // opaque: keeps the store out of the branch on `keep`
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rout, soff, 0, 0);
-    if (keep) lds_add_u32(&hist[__float_as_uint(acc) >> kHistShift], 1u);  // non-negative: bit 31 clear
+    if (keep) lds_add_u32(&hist[hist_bin(acc)], 1u);
   };
   // Iteration i: barrier (every wave's copy of K(i+1) landed, every wave done
   // with K(i)'s stage), copy K(i+NS) into that stage, QK of step i+1, then the
