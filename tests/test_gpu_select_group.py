@@ -7,7 +7,7 @@ import torch
 import sparse_attention_diffusion_amd as mcs
 from oracle import ref
 from sparse_attention_diffusion_amd import workloads as W
-from tests.gpu_util import assert_close, check_index_row, dev, host, to_dev
+from tests.gpu_util import assert_close, check_index_row, check_index_row_window, dev, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -188,12 +188,19 @@ def test_select_more_equal_masses_than_the_candidate_list_holds(dtype, kk):
         assert (idx[:, :, kk:] == -1).all()
 
 
+def _hist_bins(mass):
+    # the selection histogram's bins: exponent and top six mantissa bits of the
+    # fp32 mass over the 32 binades [2^-27, 2^5), values outside in the end bins
+    key = np.asarray(mass, np.float32).view(np.uint32).astype(np.int64) >> 17
+    return np.clip(key - (100 << 6), 0, 2047)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_select_refines_a_crowded_threshold_bin(dtype):
     # Small logits: the masses of a group lie within about 2% of each other, so
-    # nearly all 6,000 keys share one 11-bit histogram bin (1/8 relative width) and
-    # the top-K narrows the threshold with passes over the row before it can list
-    # the candidates.  Index sets against the oracle's masses.
+    # thousands of the 6,000 keys share the threshold's histogram bin (1/64 of a
+    # binade) and the top-K narrows the threshold with passes over the row before
+    # it can list the candidates.  Index sets against the oracle's masses.
     n, d, kk = 6000, 64, 1500
     r = np.random.default_rng(11)
     u = r.standard_normal(d)
@@ -205,11 +212,64 @@ def test_select_refines_a_crowded_threshold_bin(dtype):
     idx = host(mcs.mcs_select(to_dev(q, dtype), to_dev(k, dtype), torch.from_numpy(perm).to(dev()), kk))
     lse = ref.row_lse(q[0], k[0], s)
     mass = ref.group_mass(q[0], k[0], lse, perm[0], 64, s)
-    bins = np.asarray(mass[0], np.float32).view(np.uint32) >> 20  # the top 11 value bits
-    crowd = int(np.unique(bins, return_counts=True)[1].max())
+    bins = _hist_bins(mass[0])
+    tau = np.sort(mass[0])[::-1][kk - 1]
+    crowd = int((bins == _hist_bins(tau)).sum())
     ties = sum(check_index_row(idx[0, g], mass[g], kk, n) for g in range(mass.shape[0]))
-    print(f"{dtype}: {crowd} of group 0's {n} masses share one 11-bit bin; {ties} keys within the tie window")
+    print(f"{dtype}: {crowd} of group 0's {n} masses share the threshold's bin; {ties} keys within the tie window")
     assert crowd > 2048  # the construction does crowd the bin past the candidate list
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_select_threshold_in_the_top_end_bin(dtype):
+    # One key takes nearly all of every query's weight, so its group mass is close
+    # to 64: above the histogram's window, where every mass of 32 or more shares the
+    # last bin.  With K = 1 the threshold lies in that bin and the top-K narrows it
+    # from the top value bits with passes over the row.
+    n, d = 3000, 64
+    r = np.random.default_rng(21)
+    u = r.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = W.store((np.tile(4.0 * u, (n, 1)) + 0.05 * r.standard_normal((n, d)))[None], dtype)
+    k = 0.3 * r.standard_normal((n, d))
+    k[0] = 100.0 * u
+    k = W.store(k[None], dtype)
+    perm = r.permutation(n).astype(np.int32)[None]
+    s = 1.0 / np.sqrt(d)
+    idx = host(mcs.mcs_select(to_dev(q, dtype), to_dev(k, dtype), torch.from_numpy(perm).to(dev()), 1))
+    lse = ref.row_lse(q[0], k[0], s)
+    mass = ref.group_mass(q[0], k[0], lse, perm[0], 64, s)
+    assert (_hist_bins(mass.max(axis=1)) == 2047).all()  # every group's threshold is in the last bin
+    for g in range(mass.shape[0]):
+        check_index_row(idx[0, g], mass[g], 1, n)
+    assert (idx[0, :, 0] == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_select_threshold_in_the_bottom_end_bin(dtype):
+    # The first 100 keys take nearly all of the weight; every other key's group mass
+    # is about 8e-14, below the histogram's window (2^-27), where those masses share
+    # the first bin.  With K = 500 the threshold lies among them and the top-K
+    # narrows it from the top value bits.  The small masses are exp() of logits about
+    # 30 below each row's largest, so fp32 rounding of the row offsets moves them by
+    # a few 1e-6 relative: ties within 1e-4 of the threshold are accepted.
+    n, d, kk = 3000, 64, 500
+    r = np.random.default_rng(22)
+    u = r.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = W.store((np.tile(4.0 * u, (n, 1)) + 0.05 * r.standard_normal((n, d)))[None], dtype)
+    k = 0.5 * r.standard_normal((n, d))
+    k[:100] += 60.0 * u
+    k = W.store(k[None], dtype)
+    perm = r.permutation(n).astype(np.int32)[None]
+    s = 1.0 / np.sqrt(d)
+    idx = host(mcs.mcs_select(to_dev(q, dtype), to_dev(k, dtype), torch.from_numpy(perm).to(dev()), kk))
+    lse = ref.row_lse(q[0], k[0], s)
+    mass = ref.group_mass(q[0], k[0], lse, perm[0], 64, s)
+    taus = np.sort(mass, axis=1)[:, ::-1][:, kk - 1]
+    assert (_hist_bins(taus) == 0).all()  # every group's threshold is in the first bin
+    ties = sum(check_index_row_window(idx[0, g], mass[g], kk, n, 1e-4) for g in range(mass.shape[0]))
+    print(f"{dtype}: thresholds {taus.min():.3e}..{taus.max():.3e}; {ties} keys within the tie window")
 
 
 def test_select_full_density_keeps_everything():
