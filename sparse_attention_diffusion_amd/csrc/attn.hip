@@ -1191,26 +1191,56 @@ void attn_pairs_kernel(AttnArgs a, const int32_t* ncommon) {
 // ring of kDenseStages K/V stages (every group of a head reads every key in the
 // same order): each wave issues a quarter of each step's copies, and one block
 // barrier per step marks "this step's copies landed everywhere, the stage read two
-// steps ago is free".  With the K and V operands read from LDS chunk by chunk next
-// to the MFMAs that use them (not all eight chunks at once), a wave fits in 256
+// steps ago is free".  With the K and V operands read from LDS a few chunks ahead
+// of the MFMAs that use them (not all eight chunks at once), a wave fits in 256
 // registers, so two blocks share a CU and the two waves of a SIMD, from different
 // blocks, run one's exponentials beside the other's MFMAs.  Per query the
 // arithmetic is that of the one-wave-per-SIMD kernel, in the same order.
 constexpr int kDenseStages = 4;
+// LDS operand reads in flight ahead of the MFMAs: K chunks of the QK product,
+// V chunk pairs of the PV product.  With one read in flight each MFMA pair waits
+// a full LDS round trip.
+constexpr int kDenseKAhead = 3;
+constexpr int kDenseVAhead = 2;
 
-// One step of a 64-query wave on stage `cur` (no copies, no waits).
-template <int D, bool STATS, bool FIRST, bool LAST>
+// This wave's quarter of the copies of step j (K and V tiles) into its ring stage.
+template <int D, int NS>
+__device__ __forceinline__ void ring_copy(LDSP char* ring0, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int j, int ebase, uint32_t goff, int wid) {
+  constexpr int NC = LT<D>::NI / 4;
+  LDSP char* stg = ring0 + (j % NS) * LT<D>::STAGE;
+  tile_copy_dense<D, NC>(stg, rk, j, ebase, goff, wid * NC);
+  tile_copy_dense<D, NC>(stg + LT<D>::TILE, rv, j, ebase, goff, wid * NC);
+}
+
+// One step of a 64-query wave on stage `cur` (no waits).  The step's ring
+// copies (step it + NS - 1) go out right after its last V read: the compiler
+// waits for every copy in flight before a stage's first transposing read, so a
+// copy issued in this step has a whole step to land before it is waited for.
+template <int D, bool STATS, bool FIRST, bool LAST, int NS>
 __device__ __forceinline__ void rstep(LState<D, true>& st, const LCtx<D>& x, const u32x4 (&q)[2][LT<D>::KCH],
-                                      const LDSP char* cur, int it) {
+                                      const LDSP char* cur, int it, LDSP char* ring0, int wid) {
   using L = LT<D>;
   typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+  constexpr int KCH = L::KCH, KA = kDenseKAhead, VA = kDenseVAhead, NV = 2 * L::VT;
+  static_assert(KA <= KCH && VA <= NV, "read-ahead depth");
+  // QK: chunk ks + KA is read while the MFMAs of chunk ks run
   f32x16 s[2] = {f32x16{}, f32x16{}};
+  u32x4 ka[KCH];
 #pragma unroll
-  for (int ks = 0; ks < L::KCH; ++ks) {
-    const u32x4 ka = *(const LDSP u32x4*)(cur + x.kaddr[ks & 1] + 64 * (ks >> 1));
+  for (int ks = 0; ks < KA; ++ks) ka[ks] = *(const LDSP u32x4*)(cur + x.kaddr[ks & 1] + 64 * (ks >> 1));
+  __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);  // DS reads
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) s[nt] = mfma_bf16(as_bf16x8(ka), as_bf16x8(q[nt][ks]), s[nt]);
+  for (int ks = 0; ks < KCH; ++ks) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) s[nt] = mfma_bf16(as_bf16x8(ka[ks]), as_bf16x8(q[nt][ks]), s[nt]);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
+    if (ks + KA < KCH) {
+      ka[ks + KA] = *(const LDSP u32x4*)(cur + x.kaddr[(ks + KA) & 1] + 64 * ((ks + KA) >> 1));
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (LAST) lmask(s, it * 32, x.nkeys, x.hf);
   if constexpr (FIRST) {
 #pragma unroll
@@ -1223,36 +1253,41 @@ __device__ __forceinline__ void rstep(LState<D, true>& st, const LCtx<D>& x, con
   }
   uint32_t pk[2][8];
   lprobs<D, true, STATS>(st, s, pk, x.c);
+  __builtin_amdgcn_sched_barrier(0);
+  // PV: operand c = (key chunk c / VT, output tile c % VT); two transposing
+  // reads give the operand, read VA operands ahead
   const LDSP char* vt = cur + L::TILE;
+  bf16x8 vb[NV];
+  auto vread = [&](int c) {
+    const int kc = c / L::VT, n = c % L::VT;
+    const bf4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + x.vaddr[kc][0] + 64 * n));
+    const bf4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + x.vaddr[kc][1] + 64 * n));
+    vb[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-    bf16x8 pa[2];
+  for (int c = 0; c < VA; ++c) vread(c);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * VA, 0);
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    const int kc = c / L::VT, n = c % L::VT;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       u32x4 w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = pk[nt][4 * kc + i];
-      pa[nt] = as_bf16x8(w);
+      st.o[nt][n] = mfma_bf16(as_bf16x8(w), vb[c], st.o[nt][n]);
     }
-#pragma unroll
-    for (int n = 0; n < L::VT; ++n) {
-      const bf4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + x.vaddr[kc][0] + 64 * n));
-      const bf4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDSP bf4*)(vt + x.vaddr[kc][1] + 64 * n));
-      const bf16x8 vb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) st.o[nt][n] = mfma_bf16(pa[nt], vb, st.o[nt][n]);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (c + VA < NV) {
+      vread(c + VA);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    if (c + VA == NV) {
+      ring_copy<D, NS>(ring0, x.rk, x.rv, it + NS - 1, x.ebase, x.goff, wid);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * (L::NI / 4), 0);  // VMEM reads
     }
   }
-}
-
-// This wave's quarter of the copies of step j (K and V tiles) into its ring stage.
-template <int D, int NS>
-__device__ __forceinline__ void ring_copy(LDSP char* ring0, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int j, int ebase, uint32_t goff, int wid) {
-  constexpr int NC = LT<D>::NI / 4;
-  LDSP char* stg = ring0 + (j % NS) * LT<D>::STAGE;
-  tile_copy_dense<D, NC>(stg, rk, j, ebase, goff, wid * NC);
-  tile_copy_dense<D, NC>(stg + LT<D>::TILE, rv, j, ebase, goff, wid * NC);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, bool STATS>
@@ -1291,28 +1326,28 @@ void attn_dense_ring_kernel(AttnArgs a) {
   for (int j = 0; j < NS - 1; ++j) ring_copy<D, NS>(ring0, x.rk, x.rv, j, x.ebase, x.goff, wid);
   // Iteration i: this wave's copies of step i landed (those of the NS - 2 later
   // steps may still be in flight), then the barrier: everyone's have, and
-  // everyone is done with step i-1, whose stage takes step i+NS-1.  Copies run
-  // past the last step (rows past N read as zeros), so the count in flight is fixed.
-#define MCS_RING_BEGIN(i)                                                    \
+  // everyone is done with step i-1, whose stage takes step i+NS-1 (copied inside
+  // step i, after its V reads).  Copies run past the last step (rows past N read
+  // as zeros), so the count in flight is fixed.
+#define MCS_RING_BEGIN()                                                     \
   __builtin_amdgcn_sched_barrier(0);                                         \
   wait_vm<(NS - 2) * 2 * NC>();                                              \
   block_barrier();                                                           \
-  ring_copy<D, NS>(ring0, x.rk, x.rv, (i) + NS - 1, x.ebase, x.goff, wid);   \
   __builtin_amdgcn_sched_barrier(0);
   if (nsteps == 1) {
-    MCS_RING_BEGIN(0)
-    rstep<D, STATS, true, true>(st, x, q, ring0, 0);
+    MCS_RING_BEGIN()
+    rstep<D, STATS, true, true, NS>(st, x, q, ring0, 0, ring0, wid);
   } else {
-    MCS_RING_BEGIN(0)
-    rstep<D, STATS, true, false>(st, x, q, ring0, 0);
+    MCS_RING_BEGIN()
+    rstep<D, STATS, true, false, NS>(st, x, q, ring0, 0, ring0, wid);
     int it = 1;
 #pragma unroll 1
     for (; it + 1 < nsteps; ++it) {
-      MCS_RING_BEGIN(it)
-      rstep<D, STATS, false, false>(st, x, q, ring0 + (it % NS) * L::STAGE, it);
+      MCS_RING_BEGIN()
+      rstep<D, STATS, false, false, NS>(st, x, q, ring0 + (it % NS) * L::STAGE, it, ring0, wid);
     }
-    MCS_RING_BEGIN(it)
-    rstep<D, STATS, false, true>(st, x, q, ring0 + (it % NS) * L::STAGE, it);
+    MCS_RING_BEGIN()
+    rstep<D, STATS, false, true, NS>(st, x, q, ring0 + (it % NS) * L::STAGE, it, ring0, wid);
   }
 #undef MCS_RING_BEGIN
   wait_vm<0>();
