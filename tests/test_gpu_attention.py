@@ -126,6 +126,26 @@ def test_dense_is_deterministic(d):
         assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 100, 129, 200, 257])
+def test_dense_ring_short_key_lists(d, n):
+    # One to nine 32-key steps: fewer steps than the four-stage ring of the bf16
+    # dense kernel holds, a ragged last step, and blocks whose four waves are not
+    # all active (G not a multiple of 4); row statistics on and off.
+    h = 2
+    q, k, v = _qkv(h, n, d, "bf16", seed=3 * n + d, qscale=1.5)
+    s = 1.0 / np.sqrt(d)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, lse = mcs.mcs_dense_attn(qd, kd, vd, want_lse=True)
+    o2, _ = mcs.mcs_dense_attn(qd, kd, vd)
+    torch.cuda.synchronize()
+    for hh in range(h):
+        want = ref.dense_attention(q[hh], k[hh], v[hh], s)
+        assert_close(host(o)[hh], want, 2e-2, 2e-3, f"dense d{d} n{n} h{hh} (statistics)")
+        assert_close(host(o2)[hh], want, 2e-2, 2e-3, f"dense d{d} n{n} h{hh}")
+        assert_close(host(lse)[hh], ref.row_lse(q[hh], k[hh], s), 2e-4, 3e-5, f"lse d{d} n{n} h{hh}")
+
+
 @pytest.mark.parametrize("n", [192, 224, 1000])
 def test_dense_d64_many_steps(n):
     # Regression: with head_dim 64 the compiler dropped the wait for a stage's copies
