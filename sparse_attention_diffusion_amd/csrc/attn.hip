@@ -1185,13 +1185,14 @@ void attn_pairs_kernel(AttnArgs a, const int32_t* ncommon) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense attention at two blocks per CU.  A wave issues in order, so its own MFMAs
-// and its softmax VALU do not overlap; at one wave per SIMD a step costs both.
+// Dense attention at two blocks per CU.  Within a step a wave's softmax needs its
+// QK product and its PV product needs the softmax, so at one wave per SIMD a step
+// costs the MFMA time and the VALU time one after the other.
 // Here a block's four waves take four 64-query groups of one head and share a
 // ring of kDenseStages K/V stages (every group of a head reads every key in the
 // same order): each wave issues a quarter of each step's copies, and one block
-// barrier per step marks "this step's copies landed everywhere, the stage read two
-// steps ago is free".  With the K and V operands read from LDS a few chunks ahead
+// barrier per step marks "this step's copies landed everywhere, the stage read in
+// the step before is free".  With the K and V operands read from LDS a few chunks ahead
 // of the MFMAs that use them (not all eight chunks at once), a wave fits in 256
 // registers, so two blocks share a CU and the two waves of a SIMD, from different
 // blocks, run one's exponentials beside the other's MFMAs.  Per query the
