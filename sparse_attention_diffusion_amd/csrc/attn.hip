@@ -821,10 +821,10 @@ __device__ __forceinline__ void lpass(LState<D, PV>& st, const LCtx<D>& x, const
 }
 
 // Normalisation, statistics and epilogue of the LDS path.  O goes through LDS
-// (fp32, one half of the group at a time) so that every lane stores 16
-// contiguous bytes of one output row, and the residual is added in fp32 before
-// the single rounding to bf16.
-template <int D, int EPI, bool PV, bool STATS>
+// (fp32, SROWS query rows at a time; buf holds SROWS * OPITCH bytes) so that every
+// lane stores 16 contiguous bytes of one output row, and the residual is added in
+// fp32 before the single rounding to bf16.
+template <int D, int EPI, bool PV, bool STATS, int SROWS = 32>
 __device__ __forceinline__ void lfinish(const LState<D, PV>& st, const AttnArgs& a, int h, const int (&tokq)[2],
                                         const bool (&qvalid)[2], int lane, LDSP char* buf) {
   using L = LT<D>;
@@ -844,42 +844,51 @@ __device__ __forceinline__ void lfinish(const LState<D, PV>& st, const AttnArgs&
   if constexpr (PV) {
     constexpr int LPO = D / 8;        // lanes per output row (8 dims each)
     constexpr int RPO = 64 / LPO;     // rows per pass
+    static_assert(SROWS % 8 == 0 && 32 % SROWS == 0 && SROWS % RPO == 0, "staging rows");
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 8 * (r >> 2) + 4 * hf + (r & 3);
-        const float ir = lane_read(inv[nt], qi);
-#pragma unroll
-        for (int n = 0; n < L::VT; ++n)
-          *(LDSP float*)(buf + qi * L::OPITCH + (32 * n + lm) * 4) = st.o[nt][n][r] * ir;
-      }
       const int tok_l = tokq[nt], ok_l = qvalid[nt] ? 1 : 0;
       const int ch = lane % LPO;
 #pragma unroll
-      for (int p = 0; p < 32 / RPO; ++p) {
-        const int qi = p * RPO + lane / LPO;
-        const LDSP char* src = buf + qi * L::OPITCH + ch * 32;
-        const f32x4 v0 = *(const LDSP f32x4*)src;
-        const f32x4 v1 = *(const LDSP f32x4*)(src + 16);
-        const int tok = lane_read_i(tok_l, qi);
-        const int ok = lane_read_i(ok_l, qi);
-        float vals[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        if (ok) {
-          const size_t base = ((size_t)h * N + tok) * D + (size_t)ch * 8;
-          if constexpr (EPI != EPI_PLAIN) {
-            const u32x4 rw = *(const u32x4*)((const __bf16*)a.rin + base);
+      for (int hb = 0; hb < 32 / SROWS; ++hb) {
+        // accumulator register r holds row 8*(r/4) + 4*hf + r%4; the rows of this
+        // round are [hb*SROWS, (hb+1)*SROWS).  A wave's LDS accesses are done in
+        // order, so the next round's writes follow this round's reads.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float r0 = bf16lo(rw[i]), r1 = bf16hi(rw[i]);
-              vals[2 * i] = EPI == EPI_ADD ? vals[2 * i] + r0 : r0 - vals[2 * i];
-              vals[2 * i + 1] = EPI == EPI_ADD ? vals[2 * i + 1] + r1 : r1 - vals[2 * i + 1];
+        for (int r = 0; r < 16; ++r) {
+          if ((8 * (r >> 2)) / SROWS != hb) continue;
+          const int qi = 8 * (r >> 2) + 4 * hf + (r & 3);
+          const float ir = lane_read(inv[nt], qi);
+#pragma unroll
+          for (int n = 0; n < L::VT; ++n)
+            *(LDSP float*)(buf + (qi - hb * SROWS) * L::OPITCH + (32 * n + lm) * 4) = st.o[nt][n][r] * ir;
+        }
+#pragma unroll
+        for (int p = 0; p < SROWS / RPO; ++p) {
+          const int qr = p * RPO + lane / LPO;
+          const int qi = hb * SROWS + qr;
+          const LDSP char* src = buf + qr * L::OPITCH + ch * 32;
+          const f32x4 v0 = *(const LDSP f32x4*)src;
+          const f32x4 v1 = *(const LDSP f32x4*)(src + 16);
+          const int tok = lane_read_i(tok_l, qi);
+          const int ok = lane_read_i(ok_l, qi);
+          float vals[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          if (ok) {
+            const size_t base = ((size_t)h * N + tok) * D + (size_t)ch * 8;
+            if constexpr (EPI != EPI_PLAIN) {
+              const u32x4 rw = *(const u32x4*)((const __bf16*)a.rin + base);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float r0 = bf16lo(rw[i]), r1 = bf16hi(rw[i]);
+                vals[2 * i] = EPI == EPI_ADD ? vals[2 * i] + r0 : r0 - vals[2 * i];
+                vals[2 * i + 1] = EPI == EPI_ADD ? vals[2 * i + 1] + r1 : r1 - vals[2 * i + 1];
+              }
             }
-          }
-          u32x4 w;
+            u32x4 w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(vals[2 * i], vals[2 * i + 1]);
-          *(u32x4*)((__bf16*)a.o + base) = w;
+            for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(vals[2 * i], vals[2 * i + 1]);
+            *(u32x4*)((__bf16*)a.o + base) = w;
+          }
         }
       }
     }
@@ -982,7 +991,7 @@ __device__ __forceinline__ void lstate_init(LState<D, PV>& st) {
 // Normalise and store, or, if a logit far above its query's first-tile maximum
 // overflowed the fixed offset, redo the group with the online pass (direct
 // global loads over the whole key list of x.ridx).
-template <int D, bool GATHER, int EPI, bool PV, bool STATS>
+template <int D, bool GATHER, int EPI, bool PV, bool STATS, int SROWS = 32>
 __device__ __forceinline__ void lend(const LState<D, PV>& st, const LCtx<D>& x, const AttnArgs& a,
                                      __amdgpu_buffer_rsrc_t rq, int h, const int (&tokq)[2],
                                      const bool (&qvalid)[2], int lane, LDSP char* buf) {
@@ -1002,7 +1011,7 @@ __device__ __forceinline__ void lend(const LState<D, PV>& st, const LCtx<D>& x, 
     pass_online<__bf16, D, GATHER, PV, STATS>(so, xo, rq, tokq[0], tokq[1]);
     finish<__bf16, D, EPI, PV, STATS>(so, a, h, tokq, qvalid, lm, hf);
   } else {
-    lfinish<D, EPI, PV, STATS>(st, a, h, tokq, qvalid, lane, buf);
+    lfinish<D, EPI, PV, STATS, SROWS>(st, a, h, tokq, qvalid, lane, buf);
   }
 }
 
@@ -1185,30 +1194,34 @@ void attn_pairs_kernel(AttnArgs a, const int32_t* ncommon) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense attention at two blocks per CU.  Within a step a wave's softmax needs its
+// Dense attention at two waves per SIMD.  Within a step a wave's softmax needs its
 // QK product and its PV product needs the softmax, so at one wave per SIMD a step
 // costs the MFMA time and the VALU time one after the other.
-// Here a block's four waves take four 64-query groups of one head and share a
-// ring of kDenseStages K/V stages (every group of a head reads every key in the
-// same order): each wave issues a quarter of each step's copies, and one block
-// barrier per step marks "this step's copies landed everywhere, the stage read in
-// the step before is free".  With the K and V operands read from LDS a few chunks ahead
+// Here a block's waves (eight at D = 128, one block per CU; four at D = 64, two
+// blocks per CU) take consecutive 64-query groups of one head and share a ring of
+// kDenseStages K/V stages (every group of a head reads every key in the same
+// order): each wave issues its share of each step's copies, and one block barrier
+// per step marks "this step's copies landed everywhere, the stage read in the step
+// before is free".  With the K and V operands read from LDS a few chunks ahead
 // of the MFMAs that use them (not all eight chunks at once), a wave fits in 256
-// registers, so two blocks share a CU and the two waves of a SIMD, from different
-// blocks, run one's exponentials beside the other's MFMAs.  Per query the
-// arithmetic is that of the one-wave-per-SIMD kernel, in the same order.
+// registers, and the two waves of a SIMD run one's exponentials beside the other's
+// MFMAs.  Per query the arithmetic is that of the one-wave-per-SIMD kernel, in the
+// same order.
 constexpr int kDenseStages = 4;
+// Waves per block: one copy instruction of each tile per wave and step.
+template <int D>
+constexpr int dense_waves() { return LT<D>::NI >= 8 ? 8 : 4; }
 // LDS operand reads in flight ahead of the MFMAs: K chunks of the QK product,
 // V chunk pairs of the PV product.  With one read in flight each MFMA pair waits
 // a full LDS round trip.
 constexpr int kDenseKAhead = 3;
 constexpr int kDenseVAhead = 2;
 
-// This wave's quarter of the copies of step j (K and V tiles) into its ring stage.
+// This wave's share of the copies of step j (K and V tiles) into its ring stage.
 template <int D, int NS>
 __device__ __forceinline__ void ring_copy(LDSP char* ring0, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           int j, int ebase, uint32_t goff, int wid) {
-  constexpr int NC = LT<D>::NI / 4;
+  constexpr int NC = LT<D>::NI / dense_waves<D>();
   LDSP char* stg = ring0 + (j % NS) * LT<D>::STAGE;
   tile_copy_dense<D, NC>(stg, rk, j, ebase, goff, wid * NC);
   tile_copy_dense<D, NC>(stg + LT<D>::TILE, rv, j, ebase, goff, wid * NC);
@@ -1285,26 +1298,29 @@ __device__ __forceinline__ void rstep(LState<D, true>& st, const LCtx<D>& x, con
     }
     if (c + VA == NV) {
       ring_copy<D, NS>(ring0, x.rk, x.rv, it + NS - 1, x.ebase, x.goff, wid);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 * (L::NI / 4), 0);  // VMEM reads
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * (L::NI / dense_waves<D>()), 0);  // VMEM reads
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, bool STATS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__((64 * dense_waves<D>())) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_dense_ring_kernel(AttnArgs a) {
   using L = LT<D>;
-  constexpr int NS = kDenseStages;
-  constexpr int NC = L::NI / 4;
-  static_assert(NS >= 4, "the epilogue gives each wave one stage");
+  constexpr int NS = kDenseStages, W = dense_waves<D>();
+  constexpr int NC = L::NI / W;
+  // the epilogue stages SROWS query rows per wave in the ring
+  constexpr int SROWS = W == 8 ? 16 : 32;
+  static_assert(NC >= 1 && NC * W == L::NI, "copies per wave");
+  static_assert(NS * L::STAGE >= W * SROWS * L::OPITCH, "epilogue staging fits the ring");
   __shared__ __attribute__((aligned(16))) char ring[NS][L::STAGE];
   const int lane = threadIdx.x & 63, wid = wave_id();
-  const int bph = (a.G + 3) >> 2;  // blocks per head
+  const int bph = (a.G + W - 1) / W;  // blocks per head
   const int blk = xcd_remap(blockIdx.x, a.H * bph, a.xcd_chunk);
   if (blk < 0) return;  // the whole block
   const int h = blk / bph;
-  const int g = (blk - h * bph) * 4 + wid;
+  const int g = (blk - h * bph) * W + wid;
   const bool active = g < a.G;
   const int gc = active ? g : a.G - 1;  // a wave past the last group computes that group and stores nothing
   const auto rq = make_rsrc((const char*)a.q + (size_t)h * a.N * L::ROWB, (uint32_t)((size_t)a.N * L::ROWB));
@@ -1316,7 +1332,7 @@ void attn_dense_ring_kernel(AttnArgs a) {
   lqueries<D>(tokq, qvalid, q, a, rq, h, gc, lane);
   if (!active) qvalid[0] = qvalid[1] = false;
   // zero the ring before any copy lands (see lzero)
-  for (int o = (wid * 64 + lane) * 16; o < NS * L::STAGE; o += 256 * 16)
+  for (int o = (wid * 64 + lane) * 16; o < NS * L::STAGE; o += 64 * W * 16)
     *(LDSP u32x4*)((LDSP char*)&ring[0][0] + o) = u32x4{0, 0, 0, 0};
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   block_barrier();
@@ -1354,13 +1370,15 @@ void attn_dense_ring_kernel(AttnArgs a) {
   wait_vm<0>();
   block_barrier();  // every wave is done with the ring before it holds the epilogue's rows
   if (!active) return;
-  lend<D, false, EPI_PLAIN, true, STATS>(st, x, a, rq, h, tokq, qvalid, lane, ring0 + wid * L::STAGE);
+  lend<D, false, EPI_PLAIN, true, STATS, SROWS>(st, x, a, rq, h, tokq, qvalid, lane,
+                                               ring0 + wid * SROWS * L::OPITCH);
 }
 
 template <int D, bool STATS>
 hipError_t launch_dense_ring(const AttnArgs& a, hipStream_t s) {
-  const int blocks = xcd_grid(a.H * ((a.G + 3) / 4));
-  hipLaunchKernelGGL((attn_dense_ring_kernel<D, STATS>), dim3(blocks), dim3(256), 0, s, a);
+  constexpr int W = dense_waves<D>();
+  const int blocks = xcd_grid(a.H * ((a.G + W - 1) / W));
+  hipLaunchKernelGGL((attn_dense_ring_kernel<D, STATS>), dim3(blocks), dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
 
