@@ -127,11 +127,12 @@ def test_dense_is_deterministic(d):
 
 
 @pytest.mark.parametrize("d", [128, 64])
-@pytest.mark.parametrize("n", [1, 31, 32, 33, 100, 129, 200, 257])
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 100, 129, 200, 257, 600, 1100])
 def test_dense_ring_short_key_lists(d, n):
-    # One to nine 32-key steps: fewer steps than the four-stage ring of the bf16
-    # dense kernel holds, a ragged last step, and blocks whose four waves are not
-    # all active (G not a multiple of 4); row statistics on and off.
+    # One to 35 32-key steps: fewer steps than the four-stage ring of the bf16
+    # dense kernel holds, a ragged last step, and blocks whose waves (eight at
+    # D = 128, four at D = 64, one 64-query group each) are not all active;
+    # row statistics on and off.
     h = 2
     q, k, v = _qkv(h, n, d, "bf16", seed=3 * n + d, qscale=1.5)
     s = 1.0 / np.sqrt(d)
