@@ -1374,6 +1374,129 @@ void attn_dense_ring_kernel(AttnArgs a) {
                                                ring0 + wid * SROWS * L::OPITCH);
 }
 
+// ---------------------------------------------------------------------------
+// Row statistics over all keys (selection pass 1) with the dense ring: eight waves
+// of a block take eight consecutive 64-query groups of one head and share each K
+// tile (no V tile, no output).  Without O a wave needs about 128 registers, so
+// two blocks share a CU at four waves per SIMD, and each wave issues one copy
+// instruction per step.  Per query the arithmetic is that of attn_lds_kernel
+// without the PV product, in the same order.
+constexpr int kLseWaves = 8;
+
+// Copy instruction `wid` of the K tile of step j (waves past the tile's
+// instructions copy nothing).  The body exists only in the device pass: the host
+// pass of this file rejects this instantiation of tile_copy_dense (its parameter
+// substitution fails there), though the device code is the same as ring_copy's.
+template <int D, int NS>
+__device__ __forceinline__ void lse_ring_copy(LDSP char* ring0, __amdgpu_buffer_rsrc_t rk, int j, int ebase,
+                                              uint32_t goff, int wid) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NC = LT<D>::NI >= kLseWaves ? LT<D>::NI / kLseWaves : 1;
+  LDSP char* stg = ring0 + (j % NS) * LT<D>::TILE;
+  if (wid * NC < LT<D>::NI) tile_copy_dense<D, NC>(stg, rk, j, ebase, goff, wid * NC);
+#endif
+}
+
+// One step: the barrier, the copies of step it + NS - 1 into the stage read in the
+// step before, QK with the K chunks read ahead of the MFMAs, the probabilities.
+template <int D, bool FIRST, bool LAST, int NS>
+__device__ __forceinline__ void lse_ring_step(LState<D, false>& st, const LCtx<D>& x,
+                                              const u32x4 (&q)[2][LT<D>::KCH], LDSP char* ring0, int it, int wid) {
+  using L = LT<D>;
+  constexpr int NC = L::NI >= kLseWaves ? L::NI / kLseWaves : 1;
+  constexpr int KCH = L::KCH, KA = kDenseKAhead;
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's copies of step it landed once at most those of the NS - 2 later steps remain
+  wait_vm<(NS - 2) * NC>();
+  block_barrier();
+  lse_ring_copy<D, NS>(ring0, x.rk, it + NS - 1, x.ebase, x.goff, wid);
+  __builtin_amdgcn_sched_barrier(0);
+  const LDSP char* cur = ring0 + (it % NS) * L::TILE;
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  u32x4 ka[KCH];
+#pragma unroll
+  for (int ks = 0; ks < KA; ++ks) ka[ks] = *(const LDSP u32x4*)(cur + x.kaddr[ks & 1] + 64 * (ks >> 1));
+  __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
+#pragma unroll
+  for (int ks = 0; ks < KCH; ++ks) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) s[nt] = mfma_bf16(as_bf16x8(ka[ks]), as_bf16x8(q[nt][ks]), s[nt]);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (ks + KA < KCH) {
+      ka[ks + KA] = *(const LDSP u32x4*)(cur + x.kaddr[(ks + KA) & 1] + 64 * ((ks + KA) >> 1));
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LAST) lmask(s, it * 32, x.nkeys, x.hf);
+  if constexpr (FIRST) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = s[nt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+      st.m[nt] = pair_max(mx) * x.c + kMargin;
+    }
+  }
+  uint32_t pk[2][8];
+  lprobs<D, false, false>(st, s, pk, x.c);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kLseWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void attn_lse_ring_kernel(AttnArgs a) {
+  using L = LT<D>;
+  constexpr int NS = kDenseStages, W = kLseWaves;
+  __shared__ __attribute__((aligned(16))) char ring[NS][L::TILE];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int bph = (a.G + W - 1) / W;  // blocks per head
+  const int blk = xcd_remap(blockIdx.x, a.H * bph, a.xcd_chunk);
+  if (blk < 0) return;  // the whole block
+  const int h = blk / bph;
+  const int g = (blk - h * bph) * W + wid;
+  const bool active = g < a.G;
+  const int gc = active ? g : a.G - 1;  // a wave past the last group computes that group and stores nothing
+  const auto rq = make_rsrc((const char*)a.q + (size_t)h * a.N * L::ROWB, (uint32_t)((size_t)a.N * L::ROWB));
+  LCtx<D> x;
+  lctx_init<D, false>(x, a, h, gc, lane);
+  int tokq[2];
+  bool qvalid[2];
+  u32x4 q[2][L::KCH];
+  lqueries<D>(tokq, qvalid, q, a, rq, h, gc, lane);
+  if (!active) qvalid[0] = qvalid[1] = false;
+  LDSP char* ring0 = (LDSP char*)&ring[0][0];
+  // zero the ring before any copy lands (see lzero)
+  for (int o = (wid * 64 + lane) * 16; o < NS * L::TILE; o += 64 * W * 16)
+    *(LDSP u32x4*)(ring0 + o) = u32x4{0, 0, 0, 0};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  block_barrier();
+  LState<D, false> st;
+  lstate_init<D, false>(st);
+  const int nsteps = (x.nkeys + 31) >> 5;
+  for (int j = 0; j < NS - 1; ++j) lse_ring_copy<D, NS>(ring0, x.rk, j, x.ebase, x.goff, wid);
+  // copies run past the last step (rows past N read as zeros), so the count in
+  // flight is fixed
+  if (nsteps == 1) {
+    lse_ring_step<D, true, true, NS>(st, x, q, ring0, 0, wid);
+  } else {
+    lse_ring_step<D, true, false, NS>(st, x, q, ring0, 0, wid);
+    int it = 1;
+#pragma unroll 1
+    for (; it + 1 < nsteps; ++it) lse_ring_step<D, false, false, NS>(st, x, q, ring0, it, wid);
+    lse_ring_step<D, false, true, NS>(st, x, q, ring0, it, wid);
+  }
+  wait_vm<0>();  // the copies past the last step land before the block's LDS is released
+  if (!active) return;
+  lend<D, false, EPI_PLAIN, false, false>(st, x, a, rq, h, tokq, qvalid, lane, ring0);
+}
+
+template <int D>
+hipError_t launch_lse_ring(const AttnArgs& a, hipStream_t s) {
+  const int blocks = xcd_grid(a.H * ((a.G + kLseWaves - 1) / kLseWaves));
+  hipLaunchKernelGGL((attn_lse_ring_kernel<D>), dim3(blocks), dim3(64 * kLseWaves), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, bool STATS>
 hipError_t launch_dense_ring(const AttnArgs& a, hipStream_t s) {
   constexpr int W = dense_waves<D>();
@@ -1417,7 +1540,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 template <typename T, int D>
 hipError_t launch_d(const AttnArgs& a, bool gather, int epi, bool pv, hipStream_t s) {
   if constexpr (std::is_same<T, __bf16>::value) {
-    if (!pv) return gather ? launch_lds<D, true, EPI_PLAIN, false>(a, s) : launch_lds<D, false, EPI_PLAIN, false>(a, s);
+    if (!pv) return gather ? launch_lds<D, true, EPI_PLAIN, false>(a, s) : launch_lse_ring<D>(a, s);
     if (gather) {
       switch (epi) {
         case EPI_ADD: return launch_lds<D, true, EPI_ADD, true>(a, s);
