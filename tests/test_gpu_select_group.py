@@ -159,6 +159,27 @@ def test_select_matches_oracle_on_supplied_perm(grid, heads, d, dtype, rho, pass
     print(f"index entries differing within the tie window: {ties}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("n", [1, 17, 32, 33, 100, 600])
+def test_select_pass1_short_key_lists(d, n):
+    # Selection with pass 1 run by the library on one to 19 32-key steps: fewer steps
+    # than the pass-1 ring holds, a ragged last step, and blocks of eight groups
+    # with idle waves.
+    h = 2
+    r = np.random.default_rng(7 * n + d)
+    q = W.store(1.5 * r.standard_normal((h, n, d)), "bf16")
+    k = W.store(1.5 * r.standard_normal((h, n, d)), "bf16")
+    kk = max(1, n // 5)
+    s = 1.0 / np.sqrt(d)
+    perm = np.stack([r.permutation(n) for _ in range(h)]).astype(np.int32)
+    idx = host(mcs.mcs_select(to_dev(q, "bf16"), to_dev(k, "bf16"), torch.from_numpy(perm).to(dev()), kk))
+    torch.cuda.synchronize()
+    for hh in range(h):
+        mass = ref.group_mass(q[hh], k[hh], ref.row_lse(q[hh], k[hh], s), perm[hh], 64, s)
+        for gi in range(-(-n // 64)):
+            check_index_row(idx[hh, gi], mass[gi], kk, n)
+
+
 def test_select_group_of_equal_logits_ties_to_lowest_ids():
     n, d = 300, 64
     q = np.zeros((1, n, d), np.float32)
