@@ -51,6 +51,43 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(OUT, "libmcs_asan.so")
+
+
+def build_asan(verbose: bool = False) -> str:
+    """A copy of the library whose host code (the C ABI: argument checks, workspace
+    carving, launch set-up) is built with AddressSanitizer; the device code is the
+    same as in libmcs.so.  For host-side checks only: load it in a process that has
+    the clang ASan runtime (asan_runtime()) preloaded."""
+    build()
+    obj = os.path.join(OUT, "api_asan.o")
+    cmd = [HIPCC, *COMMON, "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile of api.cpp with AddressSanitizer failed:\n{r.stderr}")
+    objs = [obj] + [os.path.join(OUT, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "api.cpp"]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-shared-libasan", "-o", ASAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the AddressSanitizer library failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that hipcc links against."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    hits = sorted(glob.glob(os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so next to hipcc")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

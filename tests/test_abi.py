@@ -20,7 +20,13 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_abi.LIB_PATH):
+    # MCS_ABI_TEST_LIB: run these checks against another build of the library (the
+    # AddressSanitizer build, test_abi_asan.py)
+    other = os.environ.get("MCS_ABI_TEST_LIB")
+    if other:
+        _abi.LIB_PATH = other
+        _abi._lib = None
+    elif not os.path.exists(_abi.LIB_PATH):
         from sparse_attention_diffusion_amd import build
         build.build()
     return _abi.load()
