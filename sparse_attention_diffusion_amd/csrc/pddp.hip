@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxParts = 64;  // blocks per node at the top levels
+constexpr int kStatsAhead = 2; // tiles of gathered rows in flight per bf16 statistics block
 
 struct Node {
   int start, n;
@@ -573,24 +574,22 @@ void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) cs[i] = 0.0f;
 
+  // Rows past the part read its last row (in bounds for any tile index, padding
+  // tiles included: r1 - 1 >= nd.start) and are staged as zeros.
   auto load_toks = [&](int tile, int (&tk)[B::ITEMS]) {
 #pragma unroll
-    for (int j = 0; j < B::ITEMS; ++j) {
-      const int row = r0 + tile * B::TR + rbase + B::RSTEP * j;
-      tk[j] = row < r1 ? permh[row] : -1;
-    }
+    for (int j = 0; j < B::ITEMS; ++j) tk[j] = permh[min(r0 + tile * B::TR + rbase + B::RSTEP * j, r1 - 1)];
   };
   auto load_rows = [&](const int (&tk)[B::ITEMS], u32x4 (&xv)[B::ITEMS]) {
 #pragma unroll
-    for (int j = 0; j < B::ITEMS; ++j)
-      xv[j] = *reinterpret_cast<const u32x4*>(qh + (size_t)(tk[j] < 0 ? tok0 : tk[j]) * D + 8 * c);
+    for (int j = 0; j < B::ITEMS; ++j) xv[j] = *reinterpret_cast<const u32x4*>(qh + (size_t)tk[j] * D + 8 * c);
   };
-  auto stage = [&](LDSP char* buf, const int (&tk)[B::ITEMS], const u32x4 (&xv)[B::ITEMS]) {
+  auto stage = [&](LDSP char* buf, int tile, const u32x4 (&xv)[B::ITEMS]) {
 #pragma unroll
     for (int j = 0; j < B::ITEMS; ++j) {
       float x[8];
       chunk_to_f32<bf16>(xv[j], x);
-      const bool ok = tk[j] >= 0;  // rows past the node contribute zero
+      const bool ok = r0 + tile * B::TR + rbase + B::RSTEP * j < r1;  // rows past the part contribute zero
       u32x4 hw, lw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -639,28 +638,39 @@ void pddp_stats_bf16_kernel(PddpArgs a, Ws w, Level lv) {
     }
   };
 
-  // Tile t is read from buffer t % 2 while tile t + 1 (loaded into registers
-  // before the MFMAs) is converted into the other one; one barrier per tile.
-  int tk[B::ITEMS], tkn[B::ITEMS];
-  u32x4 xv[B::ITEMS];
-  if (ntiles > 0) {
-    load_toks(0, tk);
-    load_rows(tk, xv);
-    if (ntiles > 1) load_toks(1, tkn);
-    stage(lds, tk, xv);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) {
+  // Tile t is read from LDS buffer t % 2 while tile t + 1 is converted into the
+  // other one; one barrier per tile.  The gathered row loads run kStatsAhead
+  // tiles ahead: register slot s holds the rows of tiles s, s + A, s + 2A, ...
+  // (A = kStatsAhead), and their perm entries are read A tiles before the rows,
+  // so a wait for a tile's rows leaves the next A - 1 tiles' loads in flight
+  // (one tile in flight left the deep levels bound by the gather latency).
+  // The tile count is padded to a multiple of A with empty tiles, which stage
+  // as zeros and add nothing, so every step issues the same loads.
+  constexpr int A = kStatsAhead;
+  const int npad = (ntiles + A - 1) / A * A;
+  int tk[A][B::ITEMS];
+  u32x4 xv[A][B::ITEMS];
 #pragma unroll
-      for (int j = 0; j < B::ITEMS; ++j) tk[j] = tkn[j];
-      load_rows(tk, xv);
-      if (t + 2 < ntiles) load_toks(t + 2, tkn);
+  for (int s = 0; s < A; ++s) load_toks(s, tk[s]);
+#pragma unroll
+  for (int s = 0; s < A; ++s) {
+    load_rows(tk[s], xv[s]);
+    load_toks(s + A, tk[s]);
+  }
+  stage(lds, 0, xv[0]);
+  load_rows(tk[0], xv[0]);
+  load_toks(2 * A, tk[0]);
+  __syncthreads();
+  for (int t0 = 0; t0 < npad; t0 += A) {
+#pragma unroll
+    for (int u = 0; u < A; ++u) {
+      const int t = t0 + u, s = (u + 1) % A;  // slot of tile t + 1
+      mma_tile(lds + (t & 1) * B::BUF);
+      stage(lds + ((t + 1) & 1) * B::BUF, t + 1, xv[s]);
+      load_rows(tk[s], xv[s]);
+      load_toks(t + 1 + 2 * A, tk[s]);
+      __syncthreads();
     }
-    mma_tile(lds + (t & 1) * B::BUF);
-    if (more) stage(lds + ((t + 1) & 1) * B::BUF, tk, xv);
-    __syncthreads();
   }
 
   // Column sums: per-thread partials (tile buffers are free now), then one
